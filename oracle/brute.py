@@ -1,0 +1,110 @@
+"""Pure-Python brute-force tier for tiny inputs (oracle; test infrastructure only).
+
+Written independently of the numpy tier: explicit loops, math.exp, and the
+definitions restated directly (no shared helpers beyond the input lists).
+Used only to pin the numpy tier on tiny shapes (S <= 64, d <= 16).
+
+  position maps: [How-to] section 3 (contiguous split), [LongCtx] timeline
+  (zigzag / striped, readings as in oracle.partition);
+  visibility: [CP-TE] sections 3.3 / 5.2 and [XTuner-09] section 9.5;
+  scores and softmax: [SP-concept] section 二 (S = Q K^T / sqrt(d_k)).
+"""
+from __future__ import annotations
+
+import math
+
+
+def brute_positions(partition, S, cp, r):
+    out = []
+    sl = S // cp
+    if partition == "contiguous":
+        for i in range(sl):
+            out.append(r * sl + i)
+    elif partition == "zigzag":
+        half = S // (2 * cp)
+        for i in range(half):
+            out.append(r * half + i)
+        for i in range(half):
+            out.append((2 * cp - 1 - r) * half + i)
+    elif partition == "striped":
+        for i in range(sl):
+            out.append(r + i * cp)
+    else:
+        raise ValueError(partition)
+    return out
+
+
+def brute_doc_of(p, cu):
+    if cu is None:
+        return 0
+    for j in range(len(cu) - 1):
+        if cu[j] <= p < cu[j + 1]:
+            return j
+    raise ValueError("position outside cu_seqlens")
+
+
+def brute_attention_rank(q, k, v, cu, cp, r, partition, causal=True, scale=None):
+    """q: nested lists [S][hq][d]; k, v: [S][hkv][d]. Returns (O [R][hq][d], LSE [hq][R])."""
+    S = len(q)
+    hq = len(q[0])
+    hkv = len(k[0])
+    d = len(q[0][0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    pos = brute_positions(partition, S, cp, r)
+    O = [[[0.0] * d for _ in range(hq)] for _ in pos]
+    LSE = [[-math.inf] * len(pos) for _ in range(hq)]
+    for i, pq in enumerate(pos):
+        for h in range(hq):
+            g = (h * hkv) // hq
+            keys = []
+            for pk in range(S):
+                if causal and pk > pq:
+                    continue
+                if brute_doc_of(pk, cu) != brute_doc_of(pq, cu):
+                    continue
+                sc = 0.0
+                for c in range(d):
+                    sc += q[pq][h][c] * k[pk][g][c]
+                keys.append((pk, sc * scale))
+            if not keys:
+                continue
+            mx = max(sc for _, sc in keys)
+            tot = 0.0
+            for _, sc in keys:
+                tot += math.exp(sc - mx)
+            lse = mx + math.log(tot)
+            LSE[h][i] = lse
+            for pk, sc in keys:
+                w = math.exp(sc - lse)
+                for c in range(d):
+                    O[i][h][c] += w * v[pk][g][c]
+    return O, LSE
+
+
+def brute_classify(S, cp, r, partition, cu, bm, bn, causal=True):
+    """Nested list [CP][nqt][nkt] of 0/1/2 (skip/partial/full), by counting pairs."""
+    pos_q = brute_positions(partition, S, cp, r)
+    sl = S // cp
+    nqt = (sl + bm - 1) // bm
+    nkt = (sl + bn - 1) // bn
+    out = []
+    for t in range(cp):
+        s = (r - t) % cp
+        pos_k = brute_positions(partition, S, cp, s)
+        grid = []
+        for I in range(nqt):
+            row = []
+            for J in range(nkt):
+                n_vis = 0
+                n_all = 0
+                for i in range(I * bm, min(sl, (I + 1) * bm)):
+                    for j in range(J * bn, min(sl, (J + 1) * bn)):
+                        n_all += 1
+                        pq, pk = pos_q[i], pos_k[j]
+                        ok = (not causal or pk <= pq) and brute_doc_of(pq, cu) == brute_doc_of(pk, cu)
+                        n_vis += 1 if ok else 0
+                row.append(0 if n_vis == 0 else (2 if n_vis == n_all else 1))
+            grid.append(row)
+        out.append(grid)
+    return out
