@@ -1,0 +1,161 @@
+// C-ABI entry points of the ring-attention library (declared in include/ra.h).
+// Each call validates on the host (ra_host.cpp) before anything is launched,
+// then enqueues its kernels on the caller's stream.
+#include <math.h>
+
+#include "../../include/ra.h"
+#include "ra_common.h"
+#include "ra_host.h"
+#include "ra_internal.h"
+
+using namespace ra;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+ra_status run_forward(const void* q, const void* k, const void* v, const int32_t* cu, int32_t n_docs, int32_t cp,
+                      int32_t rank, int32_t partition, const ra_shape* shape, void* out, float* lse, float* o_steps,
+                      float* lse_steps, void* workspace, size_t ws_bytes, void* stream, bool steps) {
+  const hipStream_t st = as_stream(stream);
+  const int32_t nd = effective_docs(cu, n_docs);
+  const Layout L = attn_layout(shape, cp, nd);
+  char* ws = (char*)workspace;
+  int* dcu = nd > 1 ? (int*)(ws + L.cu_off) : nullptr;
+  int* count = (int*)(ws + L.count_off);
+  int* order = (int*)(ws + L.order_off);
+  int* wl = (int*)(ws + L.wl_off);
+  if (nd > 1 && launch_upload_i32(cu, nd + 1, dcu, st) != hipSuccess) return RA_ERR_HIP;
+  if (launch_worklist(dcu, nd, (int)shape->s_total, L.s_local, cp, rank, partition, shape->causal, L.bm, L.bn, L.nqt,
+                      L.nkt, L.wl_stride, wl, count, order, st) != hipSuccess)
+    return RA_ERR_HIP;
+  const float scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.f / sqrtf((float)shape->d);
+  AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.o_steps = o_steps;
+  a.lse_steps = lse_steps;
+  a.cu = dcu;
+  a.wl = wl;
+  a.wl_count = count;
+  a.order = order;
+  a.n_docs = nd;
+  a.s_total = (int)shape->s_total;
+  a.s_local = L.s_local;
+  a.cp = cp;
+  a.rank = rank;
+  a.part = partition;
+  a.causal = shape->causal;
+  a.hq = shape->hq;
+  a.hkv = shape->hkv;
+  a.nqt = L.nqt;
+  a.nkt = L.nkt;
+  a.wl_stride = L.wl_stride;
+  a.scale_log2 = scale * kLog2e;
+  const hipError_t e = launch_ring_attn(a, shape->d, shape->in_dtype == RA_BF16, shape->out_dtype == RA_BF16,
+                                        steps ? 1 : 0, st);
+  return e == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ra_abi_version(void) { return 1; }
+
+const char* ra_status_string(ra_status s) {
+  switch (s) {
+    case RA_OK: return "ok";
+    case RA_ERR_NULL: return "a required pointer is NULL";
+    case RA_ERR_SHAPE: return "invalid size or argument value";
+    case RA_ERR_DIVISIBILITY: return "sequence length not divisible by the CP partition";
+    case RA_ERR_HEADS: return "head count not divisible (Ulysses degree or query/KV head ratio)";
+    case RA_ERR_CU_SEQLENS: return "cu_seqlens must be 0 = c0 < c1 < ... < c_n = S";
+    case RA_ERR_RANK: return "rank outside [0, cp_size)";
+    case RA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, element size or partition";
+    case RA_ERR_WORKSPACE: return "workspace missing or smaller than ra_workspace_size()";
+    case RA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+size_t ra_workspace_size(const ra_shape* shape, int32_t cp_size, int32_t n_docs) {
+  if (!shape || shape->s_total < 1 || shape->s_total > ((int64_t)1 << 30)) return 0;
+  if (cp_size < 1 || cp_size > 64 || shape->s_total % cp_size) return 0;
+  if (shape->in_dtype != RA_BF16 && shape->in_dtype != RA_F32) return 0;
+  return attn_layout(shape, cp_size, n_docs > 1 ? n_docs : 1).total;
+}
+
+ra_status ra_forward(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_docs,
+                     int32_t cp_size, int32_t rank, int32_t partition, const ra_shape* shape, void* out, float* lse,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  const ra_status s = check_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, out, lse, workspace,
+                                    ws_bytes);
+  if (s != RA_OK) return s;
+  return run_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, out, lse, nullptr, nullptr,
+                     workspace, ws_bytes, stream, false);
+}
+
+ra_status ra_forward_steps(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_docs,
+                           int32_t cp_size, int32_t rank, int32_t partition, const ra_shape* shape, float* o_steps,
+                           float* lse_steps, void* workspace, size_t ws_bytes, void* stream) {
+  const ra_status s = check_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, o_steps, lse_steps,
+                                    workspace, ws_bytes);
+  if (s != RA_OK) return s;
+  return run_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, nullptr, nullptr, o_steps,
+                     lse_steps, workspace, ws_bytes, stream, true);
+}
+
+ra_status ra_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, const float* lse_a, const float* o_b,
+                       const float* lse_b, float* o_out, float* lse_out, void* stream) {
+  const ra_status s = check_lse_merge(rows, h, d, o_a, lse_a, o_b, lse_b, o_out, lse_out);
+  if (s != RA_OK) return s;
+  if (rows == 0) return RA_OK;
+  return launch_lse_merge(rows, h, d, o_a, lse_a, o_b, lse_b, o_out, lse_out, as_stream(stream)) == hipSuccess
+             ? RA_OK
+             : RA_ERR_HIP;
+}
+
+ra_status ra_classify(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size, int32_t rank,
+                      int32_t partition, int32_t bm, int32_t bn, int8_t* cls, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  const ra_status s =
+      check_classify(shape, cu_seqlens, n_docs, cp_size, rank, partition, bm, bn, cls, workspace, ws_bytes);
+  if (s != RA_OK) return s;
+  const hipStream_t st = as_stream(stream);
+  const int32_t nd = effective_docs(cu_seqlens, n_docs);
+  int* dcu = nd > 1 ? (int*)workspace : nullptr;
+  if (nd > 1 && launch_upload_i32(cu_seqlens, nd + 1, dcu, st) != hipSuccess) return RA_ERR_HIP;
+  const int s_local = (int)(shape->s_total / cp_size);
+  const int nqt = (s_local + bm - 1) / bm, nkt = (s_local + bn - 1) / bn;
+  return launch_classify(dcu, nd, (int)shape->s_total, s_local, cp_size, rank, partition, shape->causal, bm, bn, nqt,
+                         nkt, cls, st) == hipSuccess
+             ? RA_OK
+             : RA_ERR_HIP;
+}
+
+ra_status ulysses_permute(const void* in, void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
+                          int32_t elem_bytes, int32_t inverse, void* stream) {
+  const ra_status s = check_ulysses(in, out, n, s_local, h, d, elem_bytes, inverse);
+  if (s != RA_OK) return s;
+  const int64_t run_bytes = (int64_t)(h / n) * d * elem_bytes;
+  return launch_ulysses(in, out, n, s_local, run_bytes, inverse, as_stream(stream)) == hipSuccess ? RA_OK
+                                                                                                   : RA_ERR_HIP;
+}
+
+ra_status cp_reorder(const void* in, void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes, int32_t cp_size,
+                     int32_t partition, int32_t inverse, void* stream) {
+  const ra_status st = check_cp_reorder(in, out, s, h, d, elem_bytes, cp_size, partition, inverse);
+  if (st != RA_OK) return st;
+  const int64_t row_bytes = (int64_t)h * d * elem_bytes;
+  return launch_cp_reorder(in, out, s, row_bytes, cp_size, partition, inverse, as_stream(stream)) == hipSuccess
+             ? RA_OK
+             : RA_ERR_HIP;
+}
+
+}  // extern "C"

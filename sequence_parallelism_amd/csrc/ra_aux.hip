@@ -1,0 +1,343 @@
+// Auxiliary kernels: cu_seqlens upload, work-list construction and ordering,
+// tile classification, the standalone fp32 LSE merge, and the two local
+// permutation copies (CP reorder and Ulysses sequence<->head transpose).
+#include "ra_common.h"
+#include "ra_internal.h"
+
+namespace ra {
+
+// ---------------------------------------------------------------------------
+// cu_seqlens upload through kernel arguments (no host staging buffer, so the
+// host array may be freed as soon as the call returns).
+// ---------------------------------------------------------------------------
+struct CuChunk {
+  int n;
+  int v[kCuChunk];
+};
+
+__global__ void __launch_bounds__(256) upload_i32_kernel(const CuChunk c, int32_t* dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < c.n) dst[i] = c.v[i];
+}
+
+hipError_t launch_upload_i32(const int32_t* host, int n, int32_t* dst, hipStream_t st) {
+  for (int off = 0; off < n; off += kCuChunk) {
+    CuChunk c;
+    c.n = n - off < kCuChunk ? n - off : kCuChunk;
+    for (int i = 0; i < c.n; ++i) c.v[i] = host[off + i];
+    hipLaunchKernelGGL(upload_i32_kernel, dim3((c.n + 255) / 256), dim3(256), 0, st, c, dst + off);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Work list: for query tile I, every (ring step t, key tile J) whose class is
+// not SKIP, in step-major order, packed with its class. One block per tile.
+// ---------------------------------------------------------------------------
+struct WlArgs {
+  const int* cu;
+  int n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, wl_stride;
+  int* wl;
+  int* wl_count;
+};
+
+__global__ void __launch_bounds__(256) worklist_kernel(const WlArgs w) {
+  __shared__ int wave_tot[4];
+  const int I = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const PartInfo p{w.part, w.s_local, w.cp};
+  const int qa = I * w.bm;
+  const int qb = qa + w.bm < w.s_local ? qa + w.bm : w.s_local;
+  const int nent = w.cp * w.nkt;
+  int* out = w.wl + (size_t)I * w.wl_stride;
+  int base = 0;
+  for (int e0 = 0; e0 < nent; e0 += 256) {
+    const int e = e0 + tid;
+    int c = CLS_SKIP, t = 0, J = 0;
+    if (e < nent) {
+      t = e / w.nkt;
+      J = e - t * w.nkt;
+      const int owner = (w.rank - t + w.cp) % w.cp;
+      const int ka = J * w.bn;
+      const int kb = ka + w.bn < w.s_local ? ka + w.bn : w.s_local;
+      c = classify_tile(p, w.rank, qa, qb, owner, ka, kb, w.cu, w.n_docs, w.s_total, w.causal);
+    }
+    const unsigned long long bal = __ballot(c != CLS_SKIP);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      before += i < wave ? wave_tot[i] : 0;
+      total += wave_tot[i];
+    }
+    if (c != CLS_SKIP) out[base + before + below] = wl_pack(t, J, c);
+    base += total;
+    __syncthreads();
+  }
+  if (tid == 0) w.wl_count[I] = base;
+}
+
+// Orders query tiles by descending work (entry count), ties by index, so that
+// the longest workgroups start first.
+__global__ void __launch_bounds__(1024) order_kernel(const int* count, int nqt, int* order) {
+  __shared__ int sc[8192];
+  const bool staged = nqt <= 8192;
+  if (staged)
+    for (int i = threadIdx.x; i < nqt; i += 1024) sc[i] = count[i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < nqt; i += 1024) {
+    const int wi = staged ? sc[i] : count[i];
+    int r = 0;
+    for (int j = 0; j < nqt; ++j) {
+      const int wj = staged ? sc[j] : count[j];
+      r += (wj > wi) || (wj == wi && j < i);
+    }
+    order[r] = i;
+  }
+}
+
+hipError_t launch_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
+                           int causal, int bm, int bn, int nqt, int nkt, int wl_stride, int* wl, int* wl_count,
+                           int* order, hipStream_t st) {
+  if (nqt == 0) return hipSuccess;
+  WlArgs w{cu, n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, wl_stride, wl, wl_count};
+  hipLaunchKernelGGL(worklist_kernel, dim3(nqt), dim3(256), 0, st, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, wl_count, nqt, order);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Public tile classification: one thread per (step, query tile, key tile).
+// ---------------------------------------------------------------------------
+struct ClsArgs {
+  const int* cu;
+  int n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt;
+  int8_t* cls;
+};
+
+__global__ void __launch_bounds__(256) classify_kernel(const ClsArgs c) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long per_step = (long long)c.nqt * c.nkt;
+  if (idx >= per_step * c.cp) return;
+  const int t = (int)(idx / per_step);
+  const long long rem = idx - t * per_step;
+  const int I = (int)(rem / c.nkt), J = (int)(rem - (long long)I * c.nkt);
+  const PartInfo p{c.part, c.s_local, c.cp};
+  const int owner = (c.rank - t + c.cp) % c.cp;
+  const int qa = I * c.bm, qb = qa + c.bm < c.s_local ? qa + c.bm : c.s_local;
+  const int ka = J * c.bn, kb = ka + c.bn < c.s_local ? ka + c.bn : c.s_local;
+  c.cls[idx] = (int8_t)classify_tile(p, c.rank, qa, qb, owner, ka, kb, c.cu, c.n_docs, c.s_total, c.causal);
+}
+
+hipError_t launch_classify(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
+                           int causal, int bm, int bn, int nqt, int nkt, int8_t* cls, hipStream_t st) {
+  const long long total = (long long)cp * nqt * nkt;
+  if (total == 0) return hipSuccess;
+  ClsArgs c{cu, n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, cls};
+  hipLaunchKernelGGL(classify_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, c);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp32 LSE merge: LSE = ln(e^a + e^b), O = e^(a-LSE) O_a + e^(b-LSE) O_b.
+// A group of d/4 lanes (inside one wave) serves one (row, head): every lane of
+// the group reads both LSE values before any lane writes, so in-place calls
+// (o_out == o_a, lse_out == lse_a) are safe.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge_weights(float la, float lb, float& wa, float& wb, float& lse) {
+  const float mx = fmaxf(la, lb);
+  if (mx == -INFINITY) {
+    wa = 0.f;
+    wb = 0.f;
+    lse = -INFINITY;
+    return;
+  }
+  lse = mx + logf(expf(la - mx) + expf(lb - mx));
+  wa = expf(la - lse);
+  wb = expf(lb - lse);
+}
+
+__global__ void __launch_bounds__(256) lse_merge_vec_kernel(long long rows, int h, int d, const float* o_a,
+                                                            const float* lse_a, const float* o_b, const float* lse_b,
+                                                            float* o_out, float* lse_out) {
+  const int per = d >> 2;  // lanes per (row, head): a power of two <= 64
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long pair = gid / per;
+  const int sub = (int)(gid - pair * per);
+  if (pair >= rows * h) return;
+  const long long row = pair / h;
+  const int hh = (int)(pair - row * h);
+  const size_t li = (size_t)hh * rows + row;
+  float wa, wb, lse;
+  merge_weights(lse_a[li], lse_b[li], wa, wb, lse);
+  const size_t oi = (size_t)pair * d + 4 * sub;
+  const float4 a = *(const float4*)(o_a + oi);
+  const float4 b = *(const float4*)(o_b + oi);
+  float4 r;
+  r.x = wa * a.x + wb * b.x;
+  r.y = wa * a.y + wb * b.y;
+  r.z = wa * a.z + wb * b.z;
+  r.w = wa * a.w + wb * b.w;
+  *(float4*)(o_out + oi) = r;
+  if (sub == 0) lse_out[li] = lse;
+}
+
+__global__ void __launch_bounds__(256) lse_merge_scalar_kernel(long long rows, int h, int d, const float* o_a,
+                                                               const float* lse_a, const float* o_b,
+                                                               const float* lse_b, float* o_out, float* lse_out) {
+  const long long pair = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (pair >= rows * h) return;
+  const long long row = pair / h;
+  const int hh = (int)(pair - row * h);
+  const size_t li = (size_t)hh * rows + row;
+  float wa, wb, lse;
+  merge_weights(lse_a[li], lse_b[li], wa, wb, lse);
+  for (int c = 0; c < d; ++c) {
+    const size_t oi = (size_t)pair * d + c;
+    o_out[oi] = wa * o_a[oi] + wb * o_b[oi];
+  }
+  lse_out[li] = lse;
+}
+
+hipError_t launch_lse_merge(int64_t rows, int h, int d, const float* o_a, const float* lse_a, const float* o_b,
+                            const float* lse_b, float* o_out, float* lse_out, hipStream_t st) {
+  const long long pairs = (long long)rows * h;
+  if (pairs == 0) return hipSuccess;
+  const int per = d / 4;
+  const bool vec = d % 4 == 0 && per <= 64 && (per & (per - 1)) == 0 &&
+                   ((uintptr_t)o_a | (uintptr_t)o_b | (uintptr_t)o_out) % 16 == 0;
+  if (vec) {
+    const long long threads = pairs * per;
+    hipLaunchKernelGGL(lse_merge_vec_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rows, h, d,
+                       o_a, lse_a, o_b, lse_b, o_out, lse_out);
+  } else {
+    hipLaunchKernelGGL(lse_merge_scalar_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, st, rows, h, d,
+                       o_a, lse_a, o_b, lse_b, o_out, lse_out);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row-gather copies. Destination row R (cpr chunks of sizeof(T) bytes) is
+// copied from source row src_row(R). One wave per row; lanes stride the row.
+// ---------------------------------------------------------------------------
+enum { MAP_REORDER_FWD = 0, MAP_REORDER_INV = 1, MAP_ULY_FWD = 2, MAP_ULY_INV = 3 };
+
+struct CopyArgs {
+  const void* in;
+  void* out;
+  long long nrows;
+  long long cpr;  // chunks per row
+  int s_local;    // CP reorder: tokens per rank; Ulysses: tokens per simulated rank
+  int cp;         // CP reorder: cp size; Ulysses: n
+  int part;
+};
+
+template <int KIND>
+__device__ __forceinline__ long long src_row(const CopyArgs& c, long long R) {
+  if constexpr (KIND == MAP_REORDER_FWD) {
+    const int r = (int)(R / c.s_local), i = (int)(R - (long long)r * c.s_local);
+    return pos_of(PartInfo{c.part, c.s_local, c.cp}, r, i);
+  } else if constexpr (KIND == MAP_REORDER_INV) {
+    const int p = (int)R;
+    int r, i;
+    if (c.part == PART_CONTIGUOUS) {
+      r = p / c.s_local;
+      i = p - r * c.s_local;
+    } else if (c.part == PART_STRIPED) {
+      r = p % c.cp;
+      i = p / c.cp;
+    } else {
+      const int half = c.s_local >> 1;
+      const int ch = p / half, off = p - ch * half;
+      if (ch < c.cp) {
+        r = ch;
+        i = off;
+      } else {
+        r = 2 * c.cp - 1 - ch;
+        i = half + off;
+      }
+    }
+    return (long long)r * c.s_local + i;
+  } else if constexpr (KIND == MAP_ULY_FWD) {
+    // dst run (rho, j*s_local + i) <- src run ((j*s_local + i), rho)
+    const long long T = (long long)c.cp * c.s_local;
+    const long long rho = R / T, tok = R - rho * T;
+    return tok * c.cp + rho;
+  } else {
+    // dst run ((j*s_local + i), rho) <- src run (rho, j*s_local + i)
+    const long long T = (long long)c.cp * c.s_local;
+    const long long tok = R / c.cp, rho = R - tok * c.cp;
+    return rho * T + tok;
+  }
+}
+
+template <typename T, int KIND>
+__global__ void __launch_bounds__(256) copy_rows_kernel(const CopyArgs c) {
+  const int lane = threadIdx.x & 63;
+  const long long nw = (long long)gridDim.x * 4;
+  for (long long R = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); R < c.nrows; R += nw) {
+    const long long S = src_row<KIND>(c, R);
+    const T* src = (const T*)c.in + S * c.cpr;
+    T* dst = (T*)c.out + R * c.cpr;
+    long long i = lane;
+    for (; i + 192 < c.cpr; i += 256) {
+      const T a0 = src[i], a1 = src[i + 64], a2 = src[i + 128], a3 = src[i + 192];
+      dst[i] = a0;
+      dst[i + 64] = a1;
+      dst[i + 128] = a2;
+      dst[i + 192] = a3;
+    }
+    for (; i < c.cpr; i += 64) dst[i] = src[i];
+  }
+}
+
+template <int KIND>
+static hipError_t launch_copy(const void* in, void* out, long long nrows, long long row_bytes, int s_local, int cp,
+                              int part, hipStream_t st) {
+  if (nrows == 0 || row_bytes == 0) return hipSuccess;
+  const uintptr_t al = (uintptr_t)in | (uintptr_t)out | (uintptr_t)row_bytes;
+  long long waves = nrows;
+  long long blocks = (waves + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (al % 16 == 0) {
+    CopyArgs c{in, out, nrows, row_bytes / 16, s_local, cp, part};
+    hipLaunchKernelGGL((copy_rows_kernel<uint4, KIND>), grid, block, 0, st, c);
+  } else if (al % 8 == 0) {
+    CopyArgs c{in, out, nrows, row_bytes / 8, s_local, cp, part};
+    hipLaunchKernelGGL((copy_rows_kernel<uint2, KIND>), grid, block, 0, st, c);
+  } else if (al % 4 == 0) {
+    CopyArgs c{in, out, nrows, row_bytes / 4, s_local, cp, part};
+    hipLaunchKernelGGL((copy_rows_kernel<uint32_t, KIND>), grid, block, 0, st, c);
+  } else if (al % 2 == 0) {
+    CopyArgs c{in, out, nrows, row_bytes / 2, s_local, cp, part};
+    hipLaunchKernelGGL((copy_rows_kernel<uint16_t, KIND>), grid, block, 0, st, c);
+  } else {
+    CopyArgs c{in, out, nrows, row_bytes, s_local, cp, part};
+    hipLaunchKernelGGL((copy_rows_kernel<uint8_t, KIND>), grid, block, 0, st, c);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cp_reorder(const void* in, void* out, int64_t s, int64_t row_bytes, int cp, int part, int inverse,
+                             hipStream_t st) {
+  const int s_local = (int)(s / cp);
+  if (inverse) return launch_copy<MAP_REORDER_INV>(in, out, s, row_bytes, s_local, cp, part, st);
+  return launch_copy<MAP_REORDER_FWD>(in, out, s, row_bytes, s_local, cp, part, st);
+}
+
+hipError_t launch_ulysses(const void* in, void* out, int n, int64_t s_local, int64_t run_bytes, int inverse,
+                          hipStream_t st) {
+  const long long runs = (long long)n * n * s_local;
+  if (inverse) return launch_copy<MAP_ULY_INV>(in, out, runs, run_bytes, (int)s_local, n, 0, st);
+  return launch_copy<MAP_ULY_FWD>(in, out, runs, run_bytes, (int)s_local, n, 0, st);
+}
+
+}  // namespace ra

@@ -1,0 +1,189 @@
+// Device-side helpers shared by the ring-attention kernels (gfx950).
+//
+// Position runs: a range of a rank's local indices maps to global positions
+// that form at most two arithmetic progressions ("runs"):
+//   contiguous: pos = owner*S_l + i                    (one run, stride 1)
+//   striped:    pos = owner + cp*i                     (one run, stride cp)
+//   zigzag:     i <  S_l/2: pos = owner*half + i       (run 1, stride 1)
+//               i >= S_l/2: pos = (2cp-1-owner)*half + (i - half)   (run 2)
+// (partition definitions: ra.h, RA_PART_*; zigzag and striped are the
+// load-balancing reorders named on the long-context deep-dive page's timeline.)
+//
+// Visibility of key position pk from query position pq is the interval test
+//   lo(pq) <= pk <= hi(pq),  lo = start of pq's document,
+//   hi = pq (causal) or end of pq's document - 1 (non-causal),
+// which is the causal mask on global positions of the Context Parallelism
+// page (3.3, 5.2) restricted to pq's packed document (XTuner chapter 9.5).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+enum { PART_CONTIGUOUS = 0, PART_ZIGZAG = 1, PART_STRIPED = 2 };
+enum { CLS_SKIP = 0, CLS_PARTIAL = 1, CLS_FULL = 2 };
+
+// Work-list entry: bits 0-1 class, bits 2-7 ring step, bits 8-31 key tile.
+__host__ __device__ inline int wl_pack(int t, int J, int cls) { return (J << 8) | (t << 2) | cls; }
+__host__ __device__ inline int wl_cls(int e) { return e & 3; }
+__host__ __device__ inline int wl_step(int e) { return (e >> 2) & 63; }
+__host__ __device__ inline int wl_tile(int e) { return (int)((unsigned)e >> 8); }
+
+struct Run {
+  int start;   // global position of element 0
+  int stride;  // 1 or cp
+  int cnt;     // number of elements (0 = empty)
+  int off;     // index of element 0 within the tile
+};
+
+struct PartInfo {
+  int part;  // PART_*
+  int s_local;
+  int cp;
+};
+
+// Global position of local index i of `owner`.
+__device__ __forceinline__ int pos_of(const PartInfo& p, int owner, int i) {
+  if (p.part == PART_CONTIGUOUS) return owner * p.s_local + i;
+  if (p.part == PART_STRIPED) return owner + p.cp * i;
+  const int half = p.s_local >> 1;
+  return i < half ? owner * half + i : (2 * p.cp - 1 - owner) * half + (i - half);
+}
+
+// Runs covering local indices [a, b) of `owner`; returns the number of runs (0..2).
+__device__ __forceinline__ int runs_of(const PartInfo& p, int owner, int a, int b, Run* r) {
+  if (b <= a) return 0;
+  if (p.part == PART_CONTIGUOUS) {
+    r[0] = Run{owner * p.s_local + a, 1, b - a, 0};
+    return 1;
+  }
+  if (p.part == PART_STRIPED) {
+    r[0] = Run{owner + p.cp * a, p.cp, b - a, 0};
+    return 1;
+  }
+  const int half = p.s_local >> 1;
+  int n = 0;
+  if (a < half) {
+    const int e = b < half ? b : half;
+    r[n++] = Run{owner * half + a, 1, e - a, 0};
+  }
+  if (b > half) {
+    const int s0 = a > half ? a : half;
+    r[n++] = Run{(2 * p.cp - 1 - owner) * half + (s0 - half), 1, b - s0, s0 - a};
+  }
+  return n;
+}
+
+// Document containing position p: largest j with cu[j] <= p (cu has n_docs+1 entries).
+__device__ __forceinline__ int doc_of(const int* cu, int n_docs, int p) {
+  int lo = 0, hi = n_docs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Visible key-position interval [lo, hi] of query position pq.
+__device__ __forceinline__ void row_interval(const int* cu, int n_docs, int s_total, int causal, int pq,
+                                             int& lo, int& hi) {
+  if (n_docs <= 1) {
+    lo = 0;
+    hi = causal ? pq : s_total - 1;
+    return;
+  }
+  const int d = doc_of(cu, n_docs, pq);
+  lo = cu[d];
+  hi = causal ? pq : cu[d + 1] - 1;
+}
+
+// Indices n in [0, cnt) with A <= start + stride*n <= B, as [n0, n1] (empty if n0 > n1).
+__device__ __forceinline__ void run_range(const Run& r, int A, int B, int& n0, int& n1) {
+  if (r.cnt <= 0 || B < r.start || B < A) { n0 = 1; n1 = 0; return; }
+  const long long da = (long long)A - r.start;
+  n0 = da <= 0 ? 0 : (int)((da + r.stride - 1) / r.stride);
+  const long long nb = ((long long)B - r.start) / r.stride;
+  n1 = nb < (long long)(r.cnt - 1) ? (int)nb : r.cnt - 1;
+}
+
+__device__ __forceinline__ int doc_start_of(const int* cu, int n_docs, int p) {
+  return n_docs <= 1 ? 0 : cu[doc_of(cu, n_docs, p)];
+}
+__device__ __forceinline__ int doc_end_of(const int* cu, int n_docs, int s_total, int p) {
+  return n_docs <= 1 ? s_total : cu[doc_of(cu, n_docs, p) + 1];
+}
+
+// Exact class of the pairs (q in Q, k in K) for two runs.
+__device__ inline int classify_runs(const Run& Q, const Run& K, const int* cu, int n_docs, int s_total,
+                                    int causal) {
+  if (Q.cnt <= 0 || K.cnt <= 0) return CLS_SKIP;
+  const int qmin = Q.start, qmax = Q.start + Q.stride * (Q.cnt - 1);
+  const int kmin = K.start, kmax = K.start + K.stride * (K.cnt - 1);
+  // FULL: every k within [max_q lo(q), min_q hi(q)] = [docstart(qmax), hi(qmin)]
+  const int lo_max = doc_start_of(cu, n_docs, qmax);
+  const int hi_min = causal ? qmin : doc_end_of(cu, n_docs, s_total, qmin) - 1;
+  if (kmin >= lo_max && kmax <= hi_min) return CLS_FULL;
+  if (n_docs <= 1) return (!causal || kmin <= qmax) ? CLS_PARTIAL : CLS_SKIP;
+  // Any visible pair: some document D holds q in Q and k in K (with k <= q if causal).
+  const int dq0 = doc_of(cu, n_docs, qmin), dq1 = doc_of(cu, n_docs, qmax);
+  const int dk0 = doc_of(cu, n_docs, kmin), dk1 = doc_of(cu, n_docs, kmax);
+  const int d0 = dq0 > dk0 ? dq0 : dk0, d1 = dq1 < dk1 ? dq1 : dk1;
+  for (int D = d0; D <= d1; ++D) {
+    const int A = cu[D], B = cu[D + 1] - 1;
+    int qn0, qn1, kn0, kn1;
+    run_range(Q, A, B, qn0, qn1);
+    if (qn0 > qn1) continue;
+    run_range(K, A, B, kn0, kn1);
+    if (kn0 > kn1) continue;
+    if (!causal) return CLS_PARTIAL;
+    if (K.start + K.stride * kn0 <= Q.start + Q.stride * qn1) return CLS_PARTIAL;
+  }
+  return CLS_SKIP;
+}
+
+// Class of the tile (query rows [qa, qb) of `rank`) x (keys [ka, kb) of `owner`).
+__device__ inline int classify_tile(const PartInfo& p, int rank, int qa, int qb, int owner, int ka, int kb,
+                                    const int* cu, int n_docs, int s_total, int causal) {
+  Run qr[2], kr[2];
+  const int nq = runs_of(p, rank, qa, qb, qr);
+  const int nk = runs_of(p, owner, ka, kb, kr);
+  bool any = false, all = true;
+  for (int i = 0; i < nq; ++i)
+    for (int j = 0; j < nk; ++j) {
+      const int c = classify_runs(qr[i], kr[j], cu, n_docs, s_total, causal);
+      any |= c != CLS_SKIP;
+      all &= c == CLS_FULL;
+    }
+  if (!any) return CLS_SKIP;
+  return all ? CLS_FULL : CLS_PARTIAL;
+}
+
+// Arguments of the attention kernels (one rank, all ring steps).
+struct AttnArgs {
+  const void* q;      // [S_l][hq][d]
+  const void* k;      // [cp][S_l][hkv][d]
+  const void* v;      // [cp][S_l][hkv][d]
+  void* out;          // [S_l][hq][d] (fused mode)
+  float* lse;         // [hq][S_l]    (fused mode)
+  float* o_steps;     // [cp][S_l][hq][d] (steps mode)
+  float* lse_steps;   // [cp][hq][S_l]    (steps mode)
+  const int* cu;      // device cu_seqlens [n_docs+1] (unused when n_docs <= 1)
+  const int* wl;      // work list [nqt][wl_stride]
+  const int* wl_count;  // [nqt]
+  const int* order;   // [nqt] query tiles, heaviest first
+  int n_docs;
+  int s_total;
+  int s_local;
+  int cp;
+  int rank;
+  int part;
+  int causal;
+  int hq;
+  int hkv;
+  int nqt;
+  int nkt;
+  int wl_stride;
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+}  // namespace ra

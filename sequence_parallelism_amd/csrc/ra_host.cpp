@@ -1,0 +1,155 @@
+// Host-side validation and workspace layout. Pure C++: no HIP calls, so the
+// error paths run (and are tested) on machines without a GPU.
+#include "ra_host.h"
+
+#include <math.h>
+
+namespace ra {
+
+namespace {
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;  // positions and tile indices stay in int32
+constexpr int32_t kMaxCp = 64;                    // ring step fits the work-list entry (6 bits)
+constexpr int32_t kMaxHeads = 4096;
+
+// Tile shapes of the attention kernels (must match the device code).
+constexpr int kBf16BM = 128, kBf16BN = 64;
+constexpr int kF32BM = 64, kF32BN = 32;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool valid_partition(int32_t p) { return p == RA_PART_CONTIGUOUS || p == RA_PART_ZIGZAG || p == RA_PART_STRIPED; }
+
+ra_status check_divisible(int64_t s, int32_t cp, int32_t partition) {
+  if (partition == RA_PART_ZIGZAG) return s % (2 * (int64_t)cp) == 0 ? RA_OK : RA_ERR_DIVISIBILITY;
+  return s % cp == 0 ? RA_OK : RA_ERR_DIVISIBILITY;
+}
+
+bool overlaps(const void* a, const void* b, uint64_t bytes) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bytes && y < x + bytes;
+}
+
+}  // namespace
+
+ra_status check_shape(const ra_shape* shape, int32_t cp_size, int32_t rank, int32_t partition) {
+  if (!shape) return RA_ERR_NULL;
+  if (shape->s_total < 1 || shape->s_total > kMaxTokens) return RA_ERR_SHAPE;
+  if (shape->hq < 1 || shape->hkv < 1 || shape->hq > kMaxHeads || shape->hkv > kMaxHeads) return RA_ERR_SHAPE;
+  if (shape->causal != 0 && shape->causal != 1) return RA_ERR_SHAPE;
+  if (!(shape->softmax_scale >= 0.f) || isinf(shape->softmax_scale)) return RA_ERR_SHAPE;
+  if (cp_size < 1 || cp_size > kMaxCp) return RA_ERR_SHAPE;
+  if (!valid_partition(partition)) return RA_ERR_UNSUPPORTED;
+  if (rank < 0 || rank >= cp_size) return RA_ERR_RANK;
+  if (shape->hq % shape->hkv != 0) return RA_ERR_HEADS;
+  if (shape->d != 64 && shape->d != 128) return RA_ERR_UNSUPPORTED;
+  if (shape->in_dtype != RA_BF16 && shape->in_dtype != RA_F32) return RA_ERR_UNSUPPORTED;
+  if (shape->out_dtype != RA_BF16 && shape->out_dtype != RA_F32) return RA_ERR_UNSUPPORTED;
+  if (shape->in_dtype == RA_F32 && shape->out_dtype != RA_F32) return RA_ERR_UNSUPPORTED;
+  return check_divisible(shape->s_total, cp_size, partition);
+}
+
+ra_status check_cu(const int32_t* cu, int32_t n_docs, int64_t s_total) {
+  if (!cu) return RA_OK;
+  if (n_docs < 1 || n_docs > s_total) return RA_ERR_CU_SEQLENS;
+  if (cu[0] != 0 || cu[n_docs] != s_total) return RA_ERR_CU_SEQLENS;
+  for (int32_t i = 0; i < n_docs; ++i)
+    if (cu[i + 1] <= cu[i]) return RA_ERR_CU_SEQLENS;
+  return RA_OK;
+}
+
+int32_t effective_docs(const int32_t* cu, int32_t n_docs) { return cu ? n_docs : 1; }
+
+Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev) {
+  Layout L{};
+  L.s_local = (int)(shape->s_total / cp_size);
+  const bool bf16 = shape->in_dtype == RA_BF16;
+  L.bm = bf16 ? kBf16BM : kF32BM;
+  L.bn = bf16 ? kBf16BN : kF32BN;
+  L.nqt = (L.s_local + L.bm - 1) / L.bm;
+  L.nkt = (L.s_local + L.bn - 1) / L.bn;
+  L.wl_stride = cp_size * L.nkt;
+  L.n_docs_dev = n_docs_dev < 1 ? 1 : n_docs_dev;
+  const size_t cu_bytes = L.n_docs_dev > 1 ? (size_t)(L.n_docs_dev + 1) * 4 : 0;
+  L.cu_off = 0;
+  L.count_off = align256(L.cu_off + cu_bytes);
+  L.order_off = align256(L.count_off + (size_t)L.nqt * 4);
+  L.wl_off = align256(L.order_off + (size_t)L.nqt * 4);
+  L.total = align256(L.wl_off + (size_t)L.nqt * L.wl_stride * 4);
+  return L;
+}
+
+ra_status check_forward(const void* q, const void* k, const void* v, const int32_t* cu, int32_t n_docs,
+                        int32_t cp_size, int32_t rank, int32_t partition, const ra_shape* shape, const void* out0,
+                        const void* out1, const void* workspace, size_t ws_bytes) {
+  if (!q || !k || !v || !shape || !out0 || !out1) return RA_ERR_NULL;
+  ra_status s = check_shape(shape, cp_size, rank, partition);
+  if (s != RA_OK) return s;
+  s = check_cu(cu, n_docs, shape->s_total);
+  if (s != RA_OK) return s;
+  const Layout L = attn_layout(shape, cp_size, effective_docs(cu, n_docs));
+  if ((int64_t)L.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
+  if (!workspace || ws_bytes < L.total) return RA_ERR_WORKSPACE;
+  return RA_OK;
+}
+
+ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
+                         int32_t partition, int32_t bm, int32_t bn, const int8_t* cls, const void* workspace,
+                         size_t ws_bytes) {
+  if (!shape || !cls) return RA_ERR_NULL;
+  if (shape->s_total < 1 || shape->s_total > kMaxTokens) return RA_ERR_SHAPE;
+  if (shape->causal != 0 && shape->causal != 1) return RA_ERR_SHAPE;
+  if (cp_size < 1 || cp_size > kMaxCp) return RA_ERR_SHAPE;
+  if (!valid_partition(partition)) return RA_ERR_UNSUPPORTED;
+  if (rank < 0 || rank >= cp_size) return RA_ERR_RANK;
+  if (bm < 1 || bn < 1 || bm > 65536 || bn > 65536) return RA_ERR_SHAPE;
+  ra_status s = check_divisible(shape->s_total, cp_size, partition);
+  if (s != RA_OK) return s;
+  s = check_cu(cu, n_docs, shape->s_total);
+  if (s != RA_OK) return s;
+  const int32_t nd = effective_docs(cu, n_docs);
+  const size_t need = nd > 1 ? (size_t)(nd + 1) * 4 : 0;
+  if (need > 0 && (!workspace || ws_bytes < need)) return RA_ERR_WORKSPACE;
+  return RA_OK;
+}
+
+ra_status check_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, const float* lse_a, const float* o_b,
+                          const float* lse_b, const float* o_out, const float* lse_out) {
+  if (rows < 0 || h < 1 || d < 1) return RA_ERR_SHAPE;
+  if (rows > ((int64_t)1 << 40) / ((int64_t)h * d)) return RA_ERR_SHAPE;
+  if (rows == 0) return RA_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return RA_ERR_NULL;
+  return RA_OK;
+}
+
+ra_status check_ulysses(const void* in, const void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
+                        int32_t elem_bytes, int32_t inverse) {
+  if (!in || !out) return RA_ERR_NULL;
+  if (n < 1 || s_local < 1 || h < 1 || d < 1) return RA_ERR_SHAPE;
+  if (inverse != 0 && inverse != 1) return RA_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return RA_ERR_UNSUPPORTED;
+  if (h % n != 0) return RA_ERR_HEADS;
+  if ((int64_t)n * s_local > kMaxTokens) return RA_ERR_SHAPE;
+  const uint64_t bytes = (uint64_t)n * (uint64_t)s_local * (uint64_t)h * (uint64_t)d * (uint64_t)elem_bytes;
+  if (bytes > ((uint64_t)1 << 42)) return RA_ERR_SHAPE;
+  if (overlaps(in, out, bytes)) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+ra_status check_cp_reorder(const void* in, const void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
+                           int32_t cp_size, int32_t partition, int32_t inverse) {
+  if (!in || !out) return RA_ERR_NULL;
+  if (s < 1 || s > kMaxTokens || h < 1 || d < 1) return RA_ERR_SHAPE;
+  if (cp_size < 1 || cp_size > 65536) return RA_ERR_SHAPE;
+  if (inverse != 0 && inverse != 1) return RA_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return RA_ERR_UNSUPPORTED;
+  if (!valid_partition(partition)) return RA_ERR_UNSUPPORTED;
+  const ra_status st = check_divisible(s, cp_size, partition);
+  if (st != RA_OK) return st;
+  const uint64_t bytes = (uint64_t)s * (uint64_t)h * (uint64_t)d * (uint64_t)elem_bytes;
+  if (bytes > ((uint64_t)1 << 42)) return RA_ERR_SHAPE;
+  if (overlaps(in, out, bytes)) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+}  // namespace ra

@@ -1,0 +1,50 @@
+// Host-side argument validation and workspace layout (pure C++, no HIP calls),
+// so that every error path can be exercised on a machine without a GPU.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ra.h"
+
+namespace ra {
+
+struct Layout {
+  int s_local;
+  int bm, bn;      // attention kernel tile (query rows x keys)
+  int nqt, nkt;    // tiles along the local query / key index
+  int wl_stride;   // work-list entries reserved per query tile (cp * nkt)
+  int n_docs_dev;  // documents the kernels see (1 = no document mask)
+  size_t cu_off, count_off, order_off, wl_off, total;
+};
+
+// Shape checks shared by the attention entry points (no pointer checks).
+ra_status check_shape(const ra_shape* shape, int32_t cp_size, int32_t rank, int32_t partition);
+
+// cu_seqlens checks: NULL is one document; otherwise 0 = c0 < c1 < ... < c_n = s_total.
+ra_status check_cu(const int32_t* cu, int32_t n_docs, int64_t s_total);
+
+// Workspace layout of ra_forward / ra_forward_steps for a validated shape.
+Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev);
+
+// Number of documents the kernels see for a validated cu_seqlens argument.
+int32_t effective_docs(const int32_t* cu, int32_t n_docs);
+
+// Full validation of ra_forward / ra_forward_steps arguments.
+ra_status check_forward(const void* q, const void* k, const void* v, const int32_t* cu, int32_t n_docs,
+                        int32_t cp_size, int32_t rank, int32_t partition, const ra_shape* shape, const void* out0,
+                        const void* out1, const void* workspace, size_t ws_bytes);
+
+ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
+                         int32_t partition, int32_t bm, int32_t bn, const int8_t* cls, const void* workspace,
+                         size_t ws_bytes);
+
+ra_status check_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, const float* lse_a, const float* o_b,
+                          const float* lse_b, const float* o_out, const float* lse_out);
+
+ra_status check_ulysses(const void* in, const void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
+                        int32_t elem_bytes, int32_t inverse);
+
+ra_status check_cp_reorder(const void* in, const void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
+                           int32_t cp_size, int32_t partition, int32_t inverse);
+
+}  // namespace ra

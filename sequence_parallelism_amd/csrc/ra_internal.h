@@ -1,0 +1,42 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Tile shapes of the attention kernels (query rows x keys per work-list entry).
+constexpr int kAttnBf16BM = 128;
+constexpr int kAttnBf16BN = 64;
+constexpr int kAttnF32BM = 64;
+constexpr int kAttnF32BN = 32;
+
+// Largest batch of cu_seqlens entries passed by value to the upload kernel.
+constexpr int kCuChunk = 960;
+
+struct AttnArgs;
+
+hipError_t launch_ring_attn(const AttnArgs& a, int d, int in_bf16, int out_bf16, int steps, hipStream_t st);
+
+// Copies host cu_seqlens[0..n) into device memory dst (kernel arguments, no host staging buffer).
+hipError_t launch_upload_i32(const int32_t* host, int n, int32_t* dst, hipStream_t st);
+
+// Work list of non-SKIP (step, key tile) entries per query tile, and the tile order by work.
+hipError_t launch_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
+                           int causal, int bm, int bn, int nqt, int nkt, int wl_stride, int* wl, int* wl_count,
+                           int* order, hipStream_t st);
+
+hipError_t launch_classify(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
+                           int causal, int bm, int bn, int nqt, int nkt, int8_t* cls, hipStream_t st);
+
+hipError_t launch_lse_merge(int64_t rows, int h, int d, const float* o_a, const float* lse_a, const float* o_b,
+                            const float* lse_b, float* o_out, float* lse_out, hipStream_t st);
+
+hipError_t launch_cp_reorder(const void* in, void* out, int64_t s, int64_t row_bytes, int cp, int part, int inverse,
+                             hipStream_t st);
+
+hipError_t launch_ulysses(const void* in, void* out, int n, int64_t s_local, int64_t run_bytes, int inverse,
+                          hipStream_t st);
+
+}  // namespace ra

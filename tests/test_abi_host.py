@@ -1,0 +1,149 @@
+"""The C-ABI library loads, exports every symbol include/ra.h declares, and its
+host-side validation returns the documented error codes (CPU only: no call
+here reaches a HIP launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sequence_parallelism_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p(0x100000)           # stand-in device pointer: never dereferenced by validation
+P2 = ctypes.c_void_p(0x7f0000000000)    # far from P: no overlap
+
+
+def _lib():
+    return ra.load_library()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "ra.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(\w+)\s*\(", src, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    names = _declared_functions()
+    assert names == set(ra.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.ra_abi_version() == 1
+
+
+def test_status_strings():
+    for code in range(10):
+        assert ra.ra_status_string(code) != "unknown status"
+    assert ra.ra_status_string(99) == "unknown status"
+
+
+def shape(**kw):
+    base = dict(s_total=32768, hq=32, hkv=32, d=128, causal=True, softmax_scale=0.0,
+                in_dtype=ra.RA_BF16, out_dtype=ra.RA_BF16)
+    base.update(kw)
+    return ra.ra_shape(int(base["s_total"]), int(base["hq"]), int(base["hkv"]), int(base["d"]),
+                       int(base["causal"]), float(base["softmax_scale"]), int(base["in_dtype"]),
+                       int(base["out_dtype"]))
+
+
+def fwd(sh, cu=None, n_docs=0, cp=4, rank=0, part=1, ws=P, ws_bytes=1 << 40, q=P, out=P):
+    arr = None
+    if cu is not None:
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+    return _lib().ra_forward(q, P, P, arr, n_docs, cp, rank, part, ctypes.byref(sh), out, P, ws, ws_bytes, None)
+
+
+def test_forward_validation_codes():
+    assert fwd(shape(), q=None) == ra.RA_ERR_NULL
+    assert fwd(shape(), out=None) == ra.RA_ERR_NULL
+    assert _lib().ra_forward(P, P, P, None, 0, 4, 0, 1, None, P, P, P, 1 << 40, None) == ra.RA_ERR_NULL
+    assert fwd(shape(s_total=0)) == ra.RA_ERR_SHAPE
+    assert fwd(shape(hq=0)) == ra.RA_ERR_SHAPE
+    assert fwd(shape(causal=2)) == ra.RA_ERR_SHAPE
+    assert fwd(shape(softmax_scale=-1.0)) == ra.RA_ERR_SHAPE
+    assert fwd(shape(softmax_scale=float("nan"))) == ra.RA_ERR_SHAPE
+    assert fwd(shape(), cp=0) == ra.RA_ERR_SHAPE
+    assert fwd(shape(), cp=65) == ra.RA_ERR_SHAPE
+    assert fwd(shape(), part=3) == ra.RA_ERR_UNSUPPORTED
+    assert fwd(shape(), rank=4) == ra.RA_ERR_RANK
+    assert fwd(shape(), rank=-1) == ra.RA_ERR_RANK
+    assert fwd(shape(hq=32, hkv=6)) == ra.RA_ERR_HEADS
+    assert fwd(shape(d=96)) == ra.RA_ERR_UNSUPPORTED
+    assert fwd(shape(in_dtype=7)) == ra.RA_ERR_UNSUPPORTED
+    assert fwd(shape(in_dtype=ra.RA_F32, out_dtype=ra.RA_BF16)) == ra.RA_ERR_UNSUPPORTED
+    # divisibility: zigzag needs S % 2cp, contiguous / striped need S % cp
+    assert fwd(shape(s_total=4 * 1001), part=1) == ra.RA_ERR_DIVISIBILITY
+    assert fwd(shape(s_total=4 * 1001), part=0, ws=None, ws_bytes=0) == ra.RA_ERR_WORKSPACE
+    assert fwd(shape(s_total=4001), part=2) == ra.RA_ERR_DIVISIBILITY
+    # workspace
+    sh = shape()
+    need = ra.ra_workspace_size(sh, 4, 0)
+    assert need > 0
+    assert fwd(sh, ws=None) == ra.RA_ERR_WORKSPACE
+    assert fwd(sh, ws_bytes=need - 1) == ra.RA_ERR_WORKSPACE
+
+
+def test_cu_seqlens_validation():
+    sh = shape(s_total=64, hq=2, hkv=2)
+    good = [0, 10, 64]
+    assert fwd(sh, cu=[1, 10, 64], n_docs=2, ws_bytes=0) == ra.RA_ERR_CU_SEQLENS
+    assert fwd(sh, cu=[0, 10, 63], n_docs=2) == ra.RA_ERR_CU_SEQLENS
+    assert fwd(sh, cu=[0, 10, 10, 64], n_docs=3) == ra.RA_ERR_CU_SEQLENS
+    assert fwd(sh, cu=[0, 20, 10, 64], n_docs=3) == ra.RA_ERR_CU_SEQLENS
+    assert fwd(sh, cu=good, n_docs=0) == ra.RA_ERR_CU_SEQLENS
+    # a valid cu_seqlens with too little workspace fails on the workspace, not the documents
+    assert fwd(sh, cu=good, n_docs=2, ws_bytes=16) == ra.RA_ERR_WORKSPACE
+
+
+def test_workspace_size_grows_with_documents_and_is_zero_for_bad_shapes():
+    sh = shape()
+    a = ra.ra_workspace_size(sh, 4, 0)
+    b = ra.ra_workspace_size(sh, 4, 100)
+    assert b > a
+    assert ra.ra_workspace_size(shape(s_total=0), 4, 0) == 0
+    assert ra.ra_workspace_size(sh, 0, 0) == 0
+    assert _lib().ra_workspace_size(None, 4, 0) == 0
+
+
+def test_forward_steps_and_merge_validation():
+    lib = _lib()
+    sh = shape()
+    assert lib.ra_forward_steps(P, P, P, None, 0, 4, 0, 1, ctypes.byref(sh), None, P, P, 1 << 40, None) \
+        == ra.RA_ERR_NULL
+    assert lib.ra_forward_steps(P, P, P, None, 0, 4, 9, 1, ctypes.byref(sh), P, P, P, 1 << 40, None) \
+        == ra.RA_ERR_RANK
+    assert lib.ra_lse_merge(-1, 4, 128, P, P, P, P, P, P, None) == ra.RA_ERR_SHAPE
+    assert lib.ra_lse_merge(10, 0, 128, P, P, P, P, P, P, None) == ra.RA_ERR_SHAPE
+    assert lib.ra_lse_merge(10, 4, 128, None, P, P, P, P, P, None) == ra.RA_ERR_NULL
+    assert lib.ra_lse_merge(0, 4, 128, None, None, None, None, None, None, None) == ra.RA_OK
+
+
+def test_classify_validation():
+    lib = _lib()
+    sh = shape(s_total=4096)
+    assert lib.ra_classify(ctypes.byref(sh), None, 0, 4, 0, 1, 128, 128, None, P, 0, None) == ra.RA_ERR_NULL
+    assert lib.ra_classify(ctypes.byref(sh), None, 0, 4, 4, 1, 128, 128, P, P, 0, None) == ra.RA_ERR_RANK
+    assert lib.ra_classify(ctypes.byref(sh), None, 0, 4, 0, 1, 0, 128, P, P, 0, None) == ra.RA_ERR_SHAPE
+    assert lib.ra_classify(ctypes.byref(shape(s_total=4100)), None, 0, 4, 0, 1, 64, 64, P, P, 0, None) \
+        == ra.RA_ERR_DIVISIBILITY
+    cu = (ctypes.c_int32 * 3)(0, 100, 4096)
+    assert lib.ra_classify(ctypes.byref(sh), cu, 2, 4, 0, 1, 64, 64, P, None, 0, None) == ra.RA_ERR_WORKSPACE
+    bad = (ctypes.c_int32 * 3)(0, 5000, 4096)
+    assert lib.ra_classify(ctypes.byref(sh), bad, 2, 4, 0, 1, 64, 64, P, P, 64, None) == ra.RA_ERR_CU_SEQLENS
+
+
+def test_permute_validation():
+    lib = _lib()
+    # Ulysses: n must divide the head count (sequence_parallel_size must divide num_attention_heads)
+    assert lib.ulysses_permute(P, P2, 4, 1024, 30, 128, 2, 0, None) == ra.RA_ERR_HEADS
+    assert lib.ulysses_permute(None, P2, 4, 1024, 32, 128, 2, 0, None) == ra.RA_ERR_NULL
+    assert lib.ulysses_permute(P, P2, 0, 1024, 32, 128, 2, 0, None) == ra.RA_ERR_SHAPE
+    assert lib.ulysses_permute(P, P2, 4, 1024, 32, 128, 3, 0, None) == ra.RA_ERR_UNSUPPORTED
+    assert lib.ulysses_permute(P, P, 4, 1024, 32, 128, 2, 0, None) == ra.RA_ERR_SHAPE  # in == out
+    assert lib.cp_reorder(P, P2, 1000, 32, 128, 2, 8, 1, 0, None) == ra.RA_ERR_DIVISIBILITY
+    assert lib.cp_reorder(P, P2, 1000, 32, 128, 2, 3, 2, 0, None) == ra.RA_ERR_DIVISIBILITY
+    assert lib.cp_reorder(P, P2, 1024, 32, 128, 2, 4, 5, 0, None) == ra.RA_ERR_UNSUPPORTED
+    assert lib.cp_reorder(P, P2, 1024, 32, 128, 2, 4, 1, 2, None) == ra.RA_ERR_SHAPE
+    assert lib.cp_reorder(None, P2, 1024, 32, 128, 2, 4, 1, 0, None) == ra.RA_ERR_NULL
