@@ -36,8 +36,9 @@
  *     next rank, receive from the previous one).
  *   - Layout is thd with batch 1 ([CP-TE] 3.1): a tensor of T tokens, H heads
  *     and head_dim d is [T][H][d], row-major, d contiguous.
- *   - Positions: "partition-local order" means the order of oracle-free
- *     definition below (RA_PART_*). Masks use global positions ([CP-TE] 3.3).
+ *   - "Partition-local order" is the order in which a rank holds its global
+ *     positions under the partition (RA_PART_* below). Masks use global
+ *     positions ([CP-TE] 3.3).
  *   - Visibility of key position pk from query position pq:
  *       (causal == 0 || pk <= pq) && doc(pq) == doc(pk)
  *     where doc() comes from cu_seqlens ([XTuner-09] 9.5).
@@ -120,6 +121,23 @@ ra_status ra_forward(const void* q, const void* k, const void* v, const int32_t*
                      int32_t n_docs, int32_t cp_size, int32_t rank, int32_t partition,
                      const ra_shape* shape, void* out, float* lse, void* workspace, size_t ws_bytes,
                      void* stream);
+
+/* Planning half of ra_forward: uploads cu_seqlens and builds, in `workspace`,
+ * the per-query-tile work list of non-SKIP (ring step, key tile) pairs with
+ * their FULL / PARTIAL class ([CP-TE] 3.3) and the heaviest-first tile order.
+ * A plan depends only on (shape, cu_seqlens, cp_size, rank, partition), so
+ * one plan serves every layer that shares them. */
+ra_status ra_plan(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size,
+                  int32_t rank, int32_t partition, void* workspace, size_t ws_bytes, void* stream);
+
+/* Execution half of ra_forward: the attention kernel alone, reading the plan
+ * that ra_plan left in `workspace` (same shape, n_docs, cp_size, rank and
+ * partition; a plan made for other arguments gives undefined values but no
+ * out-of-bounds access: the kernel bounds-checks every work-list entry).
+ * Arguments as in ra_forward; cu_seqlens is not passed again. */
+ra_status ra_forward_planned(const void* q, const void* k, const void* v, int32_t n_docs, int32_t cp_size,
+                             int32_t rank, int32_t partition, const ra_shape* shape, void* out, float* lse,
+                             void* workspace, size_t ws_bytes, void* stream);
 
 /* Same inputs as ra_forward; writes each ring step's normalised partial instead
  * of the merged result:

@@ -27,7 +27,7 @@ RA_BF16, RA_F32 = 0, 1
 PARTITIONS = {"contiguous": 0, "zigzag": 1, "striped": 2}
 
 # Symbols declared in include/ra.h.
-EXPORTS = ("ra_workspace_size", "ra_forward", "ra_forward_steps", "ra_lse_merge", "ra_classify",
+EXPORTS = ("ra_workspace_size", "ra_forward", "ra_plan", "ra_forward_planned", "ra_forward_steps", "ra_lse_merge", "ra_classify",
            "ulysses_permute", "cp_reorder", "ra_status_string", "ra_abi_version")
 
 
@@ -61,6 +61,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_workspace_size.restype = sz
     lib.ra_forward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
     lib.ra_forward.restype = ctypes.c_int
+    lib.ra_plan.argtypes = [shp, vp, i32, i32, i32, i32, vp, sz, vp]
+    lib.ra_plan.restype = ctypes.c_int
+    lib.ra_forward_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
+    lib.ra_forward_planned.restype = ctypes.c_int
     lib.ra_forward_steps.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
     lib.ra_forward_steps.restype = ctypes.c_int
     lib.ra_lse_merge.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -173,6 +177,46 @@ def ra_forward(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partit
                                    _part(partition), ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(ws),
                                    ws_bytes, _stream(stream))
     _check(st, "ra_forward")
+    return out, lse
+
+
+class Plan:
+    """A work list built by ra_plan in a workspace tensor, for ra_forward_planned."""
+
+    def __init__(self, shape, n_docs, cp_size, rank, partition, workspace, ws_bytes):
+        self.shape, self.n_docs, self.cp_size, self.rank = shape, n_docs, cp_size, rank
+        self.partition, self.workspace, self.ws_bytes = partition, workspace, ws_bytes
+
+
+def ra_plan(s_total: int, hq: int, hkv: int, d: int, cu_seqlens=None, cp_size: int = 1, rank: int = 0,
+            partition="contiguous", *, causal: bool = True, softmax_scale: float = 0.0, in_dtype=None,
+            out_dtype=None, device="cuda", workspace=None, stream=None) -> Plan:
+    """Uploads cu_seqlens and builds the work list; returns a Plan for ra_forward_planned."""
+    import torch
+    in_dtype = torch.bfloat16 if in_dtype is None else in_dtype
+    out_dtype = in_dtype if out_dtype is None else out_dtype
+    shape = make_shape(s_total, hq, hkv, d, causal, softmax_scale, _dtype_code(in_dtype), _dtype_code(out_dtype))
+    cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
+    ws, ws_bytes = _workspace(shape, cp_size, n_docs, device, workspace)
+    st = load_library().ra_plan(ctypes.byref(shape), cu_ptr, n_docs, int(cp_size), int(rank), _part(partition),
+                                _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "ra_plan")
+    return Plan(shape, n_docs, int(cp_size), int(rank), _part(partition), ws, ws_bytes)
+
+
+def ra_forward_planned(q, k, v, plan: Plan, *, out=None, lse=None, stream=None):
+    """The attention kernel alone, on a Plan from ra_plan with the same shape."""
+    import torch
+    s_l, hq, d = q.shape
+    out_dtype = torch.bfloat16 if plan.shape.out_dtype == RA_BF16 else torch.float32
+    if out is None:
+        out = torch.empty((s_l, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, s_l), dtype=torch.float32, device=q.device)
+    st = load_library().ra_forward_planned(_ptr(q), _ptr(k), _ptr(v), plan.n_docs, plan.cp_size, plan.rank,
+                                           plan.partition, ctypes.byref(plan.shape), _ptr(out), _ptr(lse),
+                                           _ptr(plan.workspace), plan.ws_bytes, _stream(stream))
+    _check(st, "ra_forward_planned")
     return out, lse
 
 

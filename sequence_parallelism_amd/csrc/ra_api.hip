@@ -16,21 +16,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-ra_status run_forward(const void* q, const void* k, const void* v, const int32_t* cu, int32_t n_docs, int32_t cp,
-                      int32_t rank, int32_t partition, const ra_shape* shape, void* out, float* lse, float* o_steps,
-                      float* lse_steps, void* workspace, size_t ws_bytes, void* stream, bool steps) {
-  const hipStream_t st = as_stream(stream);
-  const int32_t nd = effective_docs(cu, n_docs);
+ra_status run_plan(const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition, const ra_shape* shape,
+                   void* workspace, hipStream_t st) {
   const Layout L = attn_layout(shape, cp, nd);
   char* ws = (char*)workspace;
   int* dcu = nd > 1 ? (int*)(ws + L.cu_off) : nullptr;
-  int* count = (int*)(ws + L.count_off);
-  int* order = (int*)(ws + L.order_off);
-  int* wl = (int*)(ws + L.wl_off);
   if (nd > 1 && launch_upload_i32(cu, nd + 1, dcu, st) != hipSuccess) return RA_ERR_HIP;
   if (launch_worklist(dcu, nd, (int)shape->s_total, L.s_local, cp, rank, partition, shape->causal, L.bm, L.bn, L.nqt,
-                      L.nkt, L.wl_stride, wl, count, order, st) != hipSuccess)
+                      L.nkt, L.wl_stride, (int*)(ws + L.wl_off), (int*)(ws + L.count_off), (int*)(ws + L.order_off),
+                      st) != hipSuccess)
     return RA_ERR_HIP;
+  return RA_OK;
+}
+
+ra_status run_attention(const void* q, const void* k, const void* v, int32_t nd, int32_t cp, int32_t rank,
+                        int32_t partition, const ra_shape* shape, void* out, float* lse, float* o_steps,
+                        float* lse_steps, void* workspace, hipStream_t st, bool steps) {
+  const Layout L = attn_layout(shape, cp, nd);
+  char* ws = (char*)workspace;
   const float scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.f / sqrtf((float)shape->d);
   AttnArgs a{};
   a.q = q;
@@ -40,10 +43,10 @@ ra_status run_forward(const void* q, const void* k, const void* v, const int32_t
   a.lse = lse;
   a.o_steps = o_steps;
   a.lse_steps = lse_steps;
-  a.cu = dcu;
-  a.wl = wl;
-  a.wl_count = count;
-  a.order = order;
+  a.cu = nd > 1 ? (const int*)(ws + L.cu_off) : nullptr;
+  a.wl = (const int*)(ws + L.wl_off);
+  a.wl_count = (const int*)(ws + L.count_off);
+  a.order = (const int*)(ws + L.order_off);
   a.n_docs = nd;
   a.s_total = (int)shape->s_total;
   a.s_local = L.s_local;
@@ -97,8 +100,30 @@ ra_status ra_forward(const void* q, const void* k, const void* v, const int32_t*
   const ra_status s = check_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, out, lse, workspace,
                                     ws_bytes);
   if (s != RA_OK) return s;
-  return run_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, out, lse, nullptr, nullptr,
-                     workspace, ws_bytes, stream, false);
+  const hipStream_t st = as_stream(stream);
+  const int32_t nd = effective_docs(cu_seqlens, n_docs);
+  const ra_status p = run_plan(cu_seqlens, nd, cp_size, rank, partition, shape, workspace, st);
+  if (p != RA_OK) return p;
+  return run_attention(q, k, v, nd, cp_size, rank, partition, shape, out, lse, nullptr, nullptr, workspace, st, false);
+}
+
+ra_status ra_plan(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size, int32_t rank,
+                  int32_t partition, void* workspace, size_t ws_bytes, void* stream) {
+  const ra_status s = check_plan(shape, cu_seqlens, n_docs, cp_size, rank, partition, workspace, ws_bytes);
+  if (s != RA_OK) return s;
+  return run_plan(cu_seqlens, effective_docs(cu_seqlens, n_docs), cp_size, rank, partition, shape, workspace,
+                  as_stream(stream));
+}
+
+ra_status ra_forward_planned(const void* q, const void* k, const void* v, int32_t n_docs, int32_t cp_size,
+                             int32_t rank, int32_t partition, const ra_shape* shape, void* out, float* lse,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  const ra_status s = check_forward_planned(q, k, v, n_docs, cp_size, rank, partition, shape, out, lse, workspace,
+                                            ws_bytes);
+  if (s != RA_OK) return s;
+  const int32_t nd = n_docs > 1 ? n_docs : 1;
+  return run_attention(q, k, v, nd, cp_size, rank, partition, shape, out, lse, nullptr, nullptr, workspace,
+                       as_stream(stream), false);
 }
 
 ra_status ra_forward_steps(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_docs,
@@ -107,8 +132,12 @@ ra_status ra_forward_steps(const void* q, const void* k, const void* v, const in
   const ra_status s = check_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, o_steps, lse_steps,
                                     workspace, ws_bytes);
   if (s != RA_OK) return s;
-  return run_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, nullptr, nullptr, o_steps,
-                     lse_steps, workspace, ws_bytes, stream, true);
+  const hipStream_t st = as_stream(stream);
+  const int32_t nd = effective_docs(cu_seqlens, n_docs);
+  const ra_status p = run_plan(cu_seqlens, nd, cp_size, rank, partition, shape, workspace, st);
+  if (p != RA_OK) return p;
+  return run_attention(q, k, v, nd, cp_size, rank, partition, shape, nullptr, nullptr, o_steps, lse_steps, workspace,
+                       st, true);
 }
 
 ra_status ra_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, const float* lse_a, const float* o_b,

@@ -62,6 +62,12 @@ __device__ __forceinline__ int head_of_slot(int hs, int hq) {
   return (hq % 8 == 0) ? (hs % 8) * (hq / 8) + hs / 8 : hs;
 }
 
+// Chunk owner visited at ring step t (any t >= 0).
+__device__ __forceinline__ int ring_owner(int rank, int t, int cp) { return ((rank - t) % cp + cp) % cp; }
+
+// Work-list length of a tile, clamped to the reserved stride.
+__device__ __forceinline__ int clamp_count(int n, int stride) { return n < 0 ? 0 : (n > stride ? stride : n); }
+
 // Per-lane visible tile-local key intervals [i0a, i1a] U [i0b, i1b] of one tile.
 struct TileMask {
   int i0a, i1a, i0b, i1b;
@@ -111,6 +117,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi32 = lane >> 5, l32 = lane & 31;
   const int qt = a.order[blockIdx.x / a.hq];
+  if (qt < 0 || qt >= a.nqt) return;  // plan made for other arguments: nothing safe to do
   const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
   const int g = h / (a.hq / a.hkv);
   const PartInfo pinfo{a.part, a.s_local, a.cp};
@@ -142,13 +149,13 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
 
   const size_t kv_row = (size_t)a.hkv * D;
   const size_t kv_chunk = (size_t)a.s_local * kv_row;
-  const int n_ent = a.wl_count[qt];
+  const int n_ent = clamp_count(a.wl_count[qt], a.wl_stride);
   const int* list = a.wl + (size_t)qt * a.wl_stride;
 
   uint4 rk[PER], rv[PER];
   auto load_tile = [&](int ent) {
     const int t = wl_step(ent), J = wl_tile(ent);
-    const int owner = (a.rank - t + a.cp) % a.cp;
+    const int owner = ring_owner(a.rank, t, a.cp);
     const __bf16* kb = (const __bf16*)a.k + owner * kv_chunk + (size_t)g * D;
     const __bf16* vb = (const __bf16*)a.v + owner * kv_chunk + (size_t)g * D;
 #pragma unroll
@@ -207,9 +214,10 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
   for (int e = 0; e < n_ent; ++e) {
     const int ent = list[e];
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
-    const int owner = (a.rank - t + a.cp) % a.cp;
+    const bool ent_ok = t < a.cp && J < a.nkt && cls != CLS_SKIP;
+    const int owner = ring_owner(a.rank, t, a.cp);
     if constexpr (STEPS) {
-      while (cur_t < t) {
+      while (ent_ok && cur_t < t) {
         flush(a.o_steps, a.lse_steps, (size_t)a.hq * a.s_local, cur_t);
 #pragma unroll
         for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
@@ -224,9 +232,9 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
     const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
     const bool ragged = kb - ka < BN;
     bool need_mask = ragged || cls == CLS_PARTIAL;
-    bool do_tile = true;
+    bool do_tile = ent_ok;
     TileMask tm{0, BN - 1, 1, 0};
-    if (need_mask) {
+    if (do_tile && need_mask) {
       tm = tile_mask(pinfo, owner, ka, kb, cls, row_ok, lo, hi);
       const bool lane_any = tm.i0a <= tm.i1a || tm.i0b <= tm.i1b;
       const bool lane_all = (tm.i0a == 0 && tm.i1a == BN - 1) || !row_ok;
@@ -349,6 +357,7 @@ __global__ void __launch_bounds__(64) ring_attn_f32_kernel(const AttnArgs a) {
 
   const int lane = threadIdx.x;
   const int qt = a.order[blockIdx.x / a.hq];
+  if (qt < 0 || qt >= a.nqt) return;
   const int h = blockIdx.x % a.hq;
   const int g = h / (a.hq / a.hkv);
   const PartInfo pinfo{a.part, a.s_local, a.cp};
@@ -369,7 +378,7 @@ __global__ void __launch_bounds__(64) ring_attn_f32_kernel(const AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const size_t kv_row = (size_t)a.hkv * D;
   const size_t kv_chunk = (size_t)a.s_local * kv_row;
-  const int n_ent = a.wl_count[qt];
+  const int n_ent = clamp_count(a.wl_count[qt], a.wl_stride);
   const int* list = a.wl + (size_t)qt * a.wl_stride;
 
   auto flush = [&](int t) {
@@ -386,7 +395,8 @@ __global__ void __launch_bounds__(64) ring_attn_f32_kernel(const AttnArgs a) {
   for (int e = 0; e < n_ent; ++e) {
     const int ent = list[e];
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
-    const int owner = (a.rank - t + a.cp) % a.cp;
+    if (t >= a.cp || J >= a.nkt || cls == CLS_SKIP) continue;  // uniform across the block
+    const int owner = ring_owner(a.rank, t, a.cp);
     if constexpr (STEPS) {
       while (cur_t < t) {
         flush(cur_t);

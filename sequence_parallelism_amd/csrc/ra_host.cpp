@@ -93,6 +93,32 @@ ra_status check_forward(const void* q, const void* k, const void* v, const int32
   return RA_OK;
 }
 
+ra_status check_plan(const ra_shape* shape, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
+                     int32_t partition, const void* workspace, size_t ws_bytes) {
+  if (!shape) return RA_ERR_NULL;
+  ra_status s = check_shape(shape, cp_size, rank, partition);
+  if (s != RA_OK) return s;
+  s = check_cu(cu, n_docs, shape->s_total);
+  if (s != RA_OK) return s;
+  const Layout L = attn_layout(shape, cp_size, effective_docs(cu, n_docs));
+  if ((int64_t)L.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
+  if (!workspace || ws_bytes < L.total) return RA_ERR_WORKSPACE;
+  return RA_OK;
+}
+
+ra_status check_forward_planned(const void* q, const void* k, const void* v, int32_t n_docs, int32_t cp_size,
+                                int32_t rank, int32_t partition, const ra_shape* shape, const void* out,
+                                const void* lse, const void* workspace, size_t ws_bytes) {
+  if (!q || !k || !v || !shape || !out || !lse) return RA_ERR_NULL;
+  ra_status s = check_shape(shape, cp_size, rank, partition);
+  if (s != RA_OK) return s;
+  if (n_docs < 0 || n_docs > shape->s_total) return RA_ERR_CU_SEQLENS;
+  const Layout L = attn_layout(shape, cp_size, n_docs > 1 ? n_docs : 1);
+  if ((int64_t)L.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
+  if (!workspace || ws_bytes < L.total) return RA_ERR_WORKSPACE;
+  return RA_OK;
+}
+
 ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
                          int32_t partition, int32_t bm, int32_t bn, const int8_t* cls, const void* workspace,
                          size_t ws_bytes) {

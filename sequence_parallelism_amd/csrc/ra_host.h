@@ -34,6 +34,15 @@ ra_status check_forward(const void* q, const void* k, const void* v, const int32
                         int32_t cp_size, int32_t rank, int32_t partition, const ra_shape* shape, const void* out0,
                         const void* out1, const void* workspace, size_t ws_bytes);
 
+// ra_plan: shape, documents and workspace (no tensor pointers).
+ra_status check_plan(const ra_shape* shape, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
+                     int32_t partition, const void* workspace, size_t ws_bytes);
+
+// ra_forward_planned: tensors, shape and workspace; n_docs as given to ra_plan.
+ra_status check_forward_planned(const void* q, const void* k, const void* v, int32_t n_docs, int32_t cp_size,
+                                int32_t rank, int32_t partition, const ra_shape* shape, const void* out,
+                                const void* lse, const void* workspace, size_t ws_bytes);
+
 ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
                          int32_t partition, int32_t bm, int32_t bn, const int8_t* cls, const void* workspace,
                          size_t ws_bytes);
