@@ -68,18 +68,17 @@ __device__ __forceinline__ int ring_owner(int rank, int t, int cp) { return ((ra
 // Work-list length of a tile, clamped to the reserved stride.
 __device__ __forceinline__ int clamp_count(int n, int stride) { return n < 0 ? 0 : (n > stride ? stride : n); }
 
-// Per-lane visible tile-local key intervals [i0a, i1a] U [i0b, i1b] of one tile.
+// Per-lane visible tile-local key indices: [i0a, i0a + la) U [i0b, i0b + lb).
 struct TileMask {
-  int i0a, i1a, i0b, i1b;
+  int i0a, la, i0b, lb;
 };
 
 __device__ __forceinline__ TileMask tile_mask(const PartInfo& p, int owner, int ka, int kb, int cls, bool row_ok,
                                               int lo, int hi) {
-  TileMask t{1, 0, 1, 0};
+  TileMask t{0, 0, 0, 0};
   if (!row_ok) return t;
   if (cls == CLS_FULL) {
-    t.i0a = 0;
-    t.i1a = kb - ka - 1;
+    t.la = kb - ka;
     return t;
   }
   Run kr[2];
@@ -88,15 +87,28 @@ __device__ __forceinline__ TileMask tile_mask(const PartInfo& p, int owner, int 
   if (nr > 0) {
     run_range(kr[0], lo, hi, n0, n1);
     t.i0a = kr[0].off + n0;
-    t.i1a = kr[0].off + n1;
+    t.la = n1 >= n0 ? n1 - n0 + 1 : 0;
   }
   if (nr > 1) {
     run_range(kr[1], lo, hi, n0, n1);
     t.i0b = kr[1].off + n0;
-    t.i1b = kr[1].off + n1;
+    t.lb = n1 >= n0 ? n1 - n0 + 1 : 0;
   }
   return t;
 }
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// The accumulator is rescaled only when a row's running max must grow by more
+// than this (log2 units): until then the stale max is kept, so P <= 2^8, which
+// bf16 P and the fp32 sums hold exactly as well; O / l is unchanged.
+constexpr float kRescaleTau = 8.0f;
 
 // ---------------------------------------------------------------------------
 // bf16 inputs, MFMA path. 4 waves x 32 query rows, key tiles of 64.
@@ -105,14 +117,17 @@ template <int D, bool OUT_BF16, bool STEPS>
 __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a) {
   constexpr int BM = kAttnBf16BM, BN = kAttnBf16BN;
   static_assert(BM == 128 && BN == 64, "tile shape is baked into the lane mapping");
-  constexpr int ROW = D + 8;                 // LDS row pitch (bf16), 16-byte aligned
-  constexpr int TILE = BN * ROW;             // one K or V tile
+  // LDS pitches (bf16): K rows read 16 B per lane down a column of rows; V rows
+  // are read by the transposing read as 4 rows x 32 B per 16 lanes.
+  constexpr int KROW = D + 8;
+  constexpr int VROW = D + 16;
+  constexpr int KTILE = BN * KROW, VTILE = BN * VROW, STAGE = KTILE + VTILE;
   constexpr int CHUNKS = BN * D / 8;         // 16-byte chunks per tile
   constexpr int PER = CHUNKS / 256;          // per thread
   constexpr int CPR = D / 8;                 // chunks per row
   constexpr int NCT = D / 32;                // 32-wide output column tiles
   constexpr int NKD = D / 16;                // 16-deep reduction steps over d
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hi32 = lane >> 5, l32 = lane & 31;
@@ -125,19 +140,14 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
   const bool row_ok = row < a.s_local;
   const float C = a.scale_log2;
 
-  // Q^T operand (B of S^T = K Q^T): lane holds q[row][16 j + 8 hi32 + 0..7].
+  // Q^T operand (B of S^T = K Q^T): lane holds q[row][16 j + 8 hi32 + 0..7]; rows past
+  // the end read as 0 through the buffer range check.
   bf16x8 qreg[NKD];
   {
-    const __bf16* qp = (const __bf16*)a.q + ((size_t)row * a.hq + h) * D + 8 * hi32;
+    const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(a.q, (uint32_t)a.s_local * a.hq * D * 2u);
+    const uint32_t qoff = ((uint32_t)row * a.hq + h) * D * 2u + 16u * hi32;
 #pragma unroll
-    for (int j = 0; j < NKD; ++j) {
-      if (row_ok) {
-        qreg[j] = *(const bf16x8*)(qp + 16 * j);
-      } else {
-        uint4 z = {0u, 0u, 0u, 0u};
-        qreg[j] = __builtin_bit_cast(bf16x8, z);
-      }
-    }
+    for (int j = 0; j < NKD; ++j) qreg[j] = __builtin_bit_cast(bf16x8, buffer_load16(qr, qoff + 32u * j));
   }
   int lo = 1, hi = 0;  // empty interval for rows past the end
   if (row_ok) row_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, a.rank, row), lo, hi);
@@ -147,48 +157,57 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
   for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  const size_t kv_row = (size_t)a.hkv * D;
-  const size_t kv_chunk = (size_t)a.s_local * kv_row;
+  const uint32_t kv_row_bytes = (uint32_t)a.hkv * D * 2u;
+  const uint32_t chunk_bytes = (uint32_t)a.s_local * kv_row_bytes;
   const int n_ent = clamp_count(a.wl_count[qt], a.wl_stride);
   const int* list = a.wl + (size_t)qt * a.wl_stride;
+
+  // per-thread byte offsets of its 16-byte chunks inside a key tile, and LDS slots
+  uint32_t goff[PER];
+  int kslot[PER], vslot[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * 256;
+    const int r = c / CPR, c8 = c % CPR;
+    goff[i] = (uint32_t)r * kv_row_bytes + ((uint32_t)g * D + c8 * 8) * 2u;
+    kslot[i] = r * KROW + c8 * 8;
+    vslot[i] = r * VROW + c8 * 8;
+  }
 
   uint4 rk[PER], rv[PER];
   auto load_tile = [&](int ent) {
     const int t = wl_step(ent), J = wl_tile(ent);
-    const int owner = ring_owner(a.rank, t, a.cp);
-    const __bf16* kb = (const __bf16*)a.k + owner * kv_chunk + (size_t)g * D;
-    const __bf16* vb = (const __bf16*)a.v + owner * kv_chunk + (size_t)g * D;
+    const size_t cbase = (size_t)ring_owner(a.rank, t, a.cp) * chunk_bytes;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc((const char*)a.k + cbase, chunk_bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc((const char*)a.v + cbase, chunk_bytes);
+    const uint32_t toff = (uint32_t)J * BN * kv_row_bytes;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * 256;
-      const int r = c / CPR, c8 = c % CPR;
-      const int j = J * BN + r;
-      if (j < a.s_local) {
-        rk[i] = *(const uint4*)(kb + (size_t)j * kv_row + c8 * 8);
-        rv[i] = *(const uint4*)(vb + (size_t)j * kv_row + c8 * 8);
-      } else {
-        rk[i] = uint4{0u, 0u, 0u, 0u};
-        rv[i] = uint4{0u, 0u, 0u, 0u};
-      }
+      rk[i] = buffer_load16(kr, toff + goff[i]);
+      rv[i] = buffer_load16(vr, toff + goff[i]);
     }
   };
   auto store_tile = [&](int buf) {
-    __bf16* ks = smem + buf * 2 * TILE;
-    __bf16* vs = ks + TILE;
+    __bf16* ks = smem + buf * STAGE;
+    __bf16* vs = ks + KTILE;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * 256;
-      const int r = c / CPR, c8 = c % CPR;
-      *(uint4*)(ks + r * ROW + c8 * 8) = rk[i];
-      *(uint4*)(vs + r * ROW + c8 * 8) = rv[i];
+      *(uint4*)(ks + kslot[i]) = rk[i];
+      *(uint4*)(vs + vslot[i]) = rv[i];
     }
   };
-  auto flush = [&](float* o_dst, float* lse_dst, size_t lse_stride_t, int t) {
-    // normalised partial of the current state (steps mode)
+  auto reset = [&]() {
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
+    m = -INFINITY;
+    l = 0.f;
+  };
+  // normalised partial of the current state (steps mode)
+  auto flush = [&](int t) {
     const float lt = swap_half_sum(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row_ok) {
-      float* op = o_dst + ((size_t)t * a.s_local * a.hq + (size_t)row * a.hq + h) * D;
+      float* op = a.o_steps + ((size_t)t * a.s_local * a.hq + (size_t)row * a.hq + h) * D;
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
 #pragma unroll
@@ -199,7 +218,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
           *(f32x4*)(op + col) = o4;
         }
       if (hi32 == 0)
-        lse_dst[t * lse_stride_t + (size_t)h * a.s_local + row] =
+        a.lse_steps[(size_t)t * a.hq * a.s_local + (size_t)h * a.s_local + row] =
             lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     }
   };
@@ -215,14 +234,10 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
     const int ent = list[e];
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
     const bool ent_ok = t < a.cp && J < a.nkt && cls != CLS_SKIP;
-    const int owner = ring_owner(a.rank, t, a.cp);
     if constexpr (STEPS) {
       while (ent_ok && cur_t < t) {
-        flush(a.o_steps, a.lse_steps, (size_t)a.hq * a.s_local, cur_t);
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
-        m = -INFINITY;
-        l = 0.f;
+        flush(cur_t);
+        reset();
         ++cur_t;
       }
     }
@@ -233,48 +248,54 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
     const bool ragged = kb - ka < BN;
     bool need_mask = ragged || cls == CLS_PARTIAL;
     bool do_tile = ent_ok;
-    TileMask tm{0, BN - 1, 1, 0};
+    TileMask tm{0, BN, 0, 0};
     if (do_tile && need_mask) {
-      tm = tile_mask(pinfo, owner, ka, kb, cls, row_ok, lo, hi);
-      const bool lane_any = tm.i0a <= tm.i1a || tm.i0b <= tm.i1b;
-      const bool lane_all = (tm.i0a == 0 && tm.i1a == BN - 1) || !row_ok;
-      do_tile = __any(lane_any);
-      need_mask = !__all(lane_all);
+      tm = tile_mask(pinfo, ring_owner(a.rank, t, a.cp), ka, kb, cls, row_ok, lo, hi);
+      do_tile = __any(tm.la > 0 || tm.lb > 0);
+      need_mask = !__all((tm.i0a == 0 && tm.la == BN) || !row_ok);
     }
 
     if (do_tile) {
-      const __bf16* ks = smem + (e & 1) * 2 * TILE;
-      const __bf16* vs = ks + TILE;
+      const __bf16* ks = smem + (e & 1) * STAGE;
+      const __bf16* vs = ks + KTILE;
       // S^T = K Q^T for 2 x 32 keys
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int j = 0; j < NKD; ++j)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 ka8 = *(const bf16x8*)(ks + (kt * 32 + l32) * ROW + 16 * j + 8 * hi32);
+          const bf16x8 ka8 = *(const bf16x8*)(ks + (kt * 32 + l32) * KROW + 16 * j + 8 * hi32);
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka8, qreg[j], s[kt], 0, 0, 0);
         }
-      // mask: lane holds keys n = 32 kt + 8 (i/4) + 4 hi32 + (i%4)
+      // mask (branch-free): lane holds keys n = 32 kt + 8 (i/4) + 4 hi32 + (i%4)
       if (need_mask) {
+        const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int n = kt * 32 + 8 * (i >> 2) + 4 * hi32 + (i & 3);
-            const bool vis = (n >= tm.i0a && n <= tm.i1a) || (n >= tm.i0b && n <= tm.i1b);
+            const int n = kt * 32 + 8 * (i >> 2) + (i & 3);
+            const bool vis = ((unsigned)(n + ba) < (unsigned)tm.la) | ((unsigned)(n + bb) < (unsigned)tm.lb);
             s[kt][i] = vis ? s[kt][i] : -INFINITY;
           }
       }
-      // online softmax (log2 domain)
+      // online softmax in the log2 domain, lazy rescale
       float mx = s[0][0];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-      mx = swap_half_max(mx);
-      const float m_new = fmaxf(m, mx * C);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      mx = swap_half_max(mx) * C;
+      const bool grow = mx > m + kRescaleTau;
+      if (__any(grow)) {
+        // rows that do not grow keep alpha = 1 exactly (their m may still be -inf)
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) acc[c] *= alpha;
+        m = grow ? mx : m;
+      }
+      const float m_use = m == -INFINITY ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -284,10 +305,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
           s[kt][i] = p;
           rs += p;
         }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int c = 0; c < NCT; ++c) acc[c] *= alpha;
+      l += rs;
       // O^T += V^T P^T
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -299,8 +317,8 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
           for (int jj = 0; jj < 2; ++jj) {
             const int r0 = kt * 32 + jj * 16 + 4 * hi32 + ((lane & 15) >> 2);
             const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            const bf16x4 v0 = lds_read_tr(vs + r0 * ROW + c0);
-            const bf16x4 v1 = lds_read_tr(vs + (r0 + 8) * ROW + c0);
+            const bf16x4 v0 = lds_read_tr(vs + r0 * VROW + c0);
+            const bf16x4 v1 = lds_read_tr(vs + (r0 + 8) * VROW + c0);
             const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
             acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, jj ? pb1 : pb0, acc[c], 0, 0, 0);
           }
@@ -313,11 +331,8 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
 
   if constexpr (STEPS) {
     while (cur_t < a.cp) {
-      flush(a.o_steps, a.lse_steps, (size_t)a.hq * a.s_local, cur_t);
-#pragma unroll
-      for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
-      m = -INFINITY;
-      l = 0.f;
+      flush(cur_t);
+      reset();
       ++cur_t;
     }
   } else {
@@ -432,7 +447,7 @@ __global__ void __launch_bounds__(64) ring_attn_f32_kernel(const AttnArgs a) {
       float dot = 0.f;
 #pragma unroll
       for (int c = 0; c < D; ++c) dot = __builtin_fmaf(qs[lane][c], ks[j][c], dot);
-      const bool vis = (j >= tm.i0a && j <= tm.i1a) || (j >= tm.i0b && j <= tm.i1b);
+      const bool vis = ((unsigned)(j - tm.i0a) < (unsigned)tm.la) | ((unsigned)(j - tm.i0b) < (unsigned)tm.lb);
       s[j] = vis ? dot : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }

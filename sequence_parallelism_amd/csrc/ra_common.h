@@ -98,12 +98,20 @@ __device__ __forceinline__ void row_interval(const int* cu, int n_docs, int s_to
 }
 
 // Indices n in [0, cnt) with A <= start + stride*n <= B, as [n0, n1] (empty if n0 > n1).
+// Positions stay below 2^30, so 32-bit differences cannot overflow.
 __device__ __forceinline__ void run_range(const Run& r, int A, int B, int& n0, int& n1) {
-  if (r.cnt <= 0 || B < r.start || B < A) { n0 = 1; n1 = 0; return; }
-  const long long da = (long long)A - r.start;
-  n0 = da <= 0 ? 0 : (int)((da + r.stride - 1) / r.stride);
-  const long long nb = ((long long)B - r.start) / r.stride;
-  n1 = nb < (long long)(r.cnt - 1) ? (int)nb : r.cnt - 1;
+  if (r.cnt <= 0 || B < A || B < r.start) { n0 = 1; n1 = 0; return; }
+  const int da = A - r.start;
+  const int db = B - r.start;
+  if (r.stride == 1) {
+    n0 = da <= 0 ? 0 : da;
+    n1 = db < r.cnt - 1 ? db : r.cnt - 1;
+  } else {
+    const unsigned st = (unsigned)r.stride;
+    n0 = da <= 0 ? 0 : (int)(((unsigned)da + st - 1u) / st);
+    const int nb = (int)((unsigned)db / st);
+    n1 = nb < r.cnt - 1 ? nb : r.cnt - 1;
+  }
 }
 
 __device__ __forceinline__ int doc_start_of(const int* cu, int n_docs, int p) {

@@ -46,7 +46,13 @@ ra_status check_shape(const ra_shape* shape, int32_t cp_size, int32_t rank, int3
   if (shape->in_dtype != RA_BF16 && shape->in_dtype != RA_F32) return RA_ERR_UNSUPPORTED;
   if (shape->out_dtype != RA_BF16 && shape->out_dtype != RA_F32) return RA_ERR_UNSUPPORTED;
   if (shape->in_dtype == RA_F32 && shape->out_dtype != RA_F32) return RA_ERR_UNSUPPORTED;
-  return check_divisible(shape->s_total, cp_size, partition);
+  const ra_status st = check_divisible(shape->s_total, cp_size, partition);
+  if (st != RA_OK) return st;
+  // the kernels address one rank's Q and one K/V chunk with 32-bit byte offsets
+  const int64_t heads = shape->hq > shape->hkv ? shape->hq : shape->hkv;
+  const int64_t elem = shape->in_dtype == RA_BF16 ? 2 : 4;
+  if ((shape->s_total / cp_size) * heads * shape->d * elem > 0x7fffffffLL) return RA_ERR_SHAPE;
+  return RA_OK;
 }
 
 ra_status check_cu(const int32_t* cu, int32_t n_docs, int64_t s_total) {

@@ -126,7 +126,11 @@ def test_steps_partials_and_merge_chain():
     out, lse = ra.ra_forward(qr, kr, vr, g.cu_seqlens, cp, rank, part, out_dtype=torch.float32)
     O, L = oracle.attention_rank(gq, gk, gv, g.cu_seqlens, cp, rank, part)
     assert max_abs(o.cpu().numpy(), O) <= TOL_O_BF16 and max_abs(l.cpu().numpy(), L) <= TOL_LSE_BF16
-    assert max_abs(o.cpu().numpy(), out.cpu().numpy()) <= 1e-3
+    # The two paths round P to bf16 (relative 2^-9) against different running maxima
+    # (per step vs carried across steps), so O may differ by about 2 * 2^-9 * max|O|.
+    # LSE does not depend on the rounding of P.
+    bound = 2 * 2.0 ** -9 * max(1.0, float(np.abs(O).max()))
+    assert max_abs(o.cpu().numpy(), out.cpu().numpy()) <= bound
     assert max_abs(l.cpu().numpy(), lse.cpu().numpy()) <= 1e-4
 
 
