@@ -205,10 +205,10 @@ def main():
         ra.cp_reorder(q_g, cp, w.partition, out=q_p)
         ra.cp_reorder(k_g, cp, w.partition, out=k_p)
         ra.cp_reorder(v_g, cp, w.partition, out=v_p)
-        for _ in range(5):
+        for _ in range(12):
             ra.ra_forward_planned(q_p[rank], k_p, v_p, plan, out=out, lse=lse)
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "attn-only", "launches": 5, "flops_per_launch": flops}))
+        print(json.dumps({"mode": "attn-only", "launches": 12, "flops_per_launch": flops}))
         return
 
     def step():
@@ -351,6 +351,15 @@ def extras(np, torch, ra, synth, dev, reps):
                          "tflops": fl / (tr["avg_ms"] * 1e-3) / 1e12})
     heavy = max(per_rank, key=lambda x: x["flops"])
     res["ring_attn_packed_docs_zigzag"] = {"n_docs": len(cu) - 1, "max_work_rank": heavy, "ranks": per_rank}
+
+    # measured copy ceiling: torch's device-to-device copy of 1 GiB
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    tc = time_events(torch, lambda: dst.copy_(src), reps)
+    nbytes = 2 * src.numel() * 2
+    res["reference_torch_copy_1GiB"] = {"avg_ms": tc["avg_ms"], "bytes": nbytes,
+                                        "gbs": nbytes / (tc["avg_ms"] * 1e-3) / 1e9}
+    del src, dst
 
     # fp32 LSE merge of two [8192, 32, 128] partials (HBM-bound)
     rows, h, dd = 8192, 32, 128

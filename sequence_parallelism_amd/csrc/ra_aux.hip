@@ -298,13 +298,70 @@ __global__ void __launch_bounds__(256) copy_rows_kernel(const CopyArgs c) {
   }
 }
 
-template <int KIND>
+// 16-byte chunks, rows of a power-of-two number of chunks (at most 1024): the
+// destination is walked as one flat array of chunks, each thread keeping
+// kCopyUnroll loads in flight; row and column come from shifts.
+constexpr int kCopyUnroll = 4;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// SCATTER: walk the source in order and send row R to destination row map(R)
+// (map is then the inverse permutation); otherwise walk the destination and
+// gather destination row R from source row map(R).
+template <int KIND, bool SCATTER>
+__global__ void __launch_bounds__(256) copy_rows_pow2_kernel(const CopyArgs c, int log2_cpr) {
+  const u32x4* src = (const u32x4*)c.in;
+  u32x4* dst = (u32x4*)c.out;
+  const long long total = c.nrows << log2_cpr;
+  const long long cmask = (1ll << log2_cpr) - 1;
+  const long long step = (long long)gridDim.x * 256 * kCopyUnroll;
+  for (long long base = (long long)blockIdx.x * 256 * kCopyUnroll + threadIdx.x; base < total; base += step) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const long long idx = base + u * 256;
+      if (idx < total) {
+        if constexpr (SCATTER) {
+          v[u] = __builtin_nontemporal_load(src + idx);
+        } else {
+          const long long R = idx >> log2_cpr;
+          v[u] = __builtin_nontemporal_load(src + ((src_row<KIND>(c, R) << log2_cpr) | (idx & cmask)));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const long long idx = base + u * 256;
+      if (idx < total) {
+        if constexpr (SCATTER) {
+          const long long R = idx >> log2_cpr;
+          __builtin_nontemporal_store(v[u], dst + ((src_row<KIND>(c, R) << log2_cpr) | (idx & cmask)));
+        } else {
+          __builtin_nontemporal_store(v[u], dst + idx);
+        }
+      }
+    }
+  }
+}
+
+template <int KIND, bool SCATTER = false>
 static hipError_t launch_copy(const void* in, void* out, long long nrows, long long row_bytes, int s_local, int cp,
                               int part, hipStream_t st) {
   if (nrows == 0 || row_bytes == 0) return hipSuccess;
   const uintptr_t al = (uintptr_t)in | (uintptr_t)out | (uintptr_t)row_bytes;
-  long long waves = nrows;
-  long long blocks = (waves + 3) / 4;
+  const long long cpr16 = row_bytes / 16;
+  if (al % 16 == 0 && cpr16 <= 1024 && (cpr16 & (cpr16 - 1)) == 0) {
+    int lg = 0;
+    while ((1ll << lg) < cpr16) ++lg;
+    const long long chunks = nrows * cpr16;
+    long long blocks = (chunks + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
+    if (blocks > 65536) blocks = 65536;
+    CopyArgs c{in, out, nrows, cpr16, s_local, cp, part};
+    hipLaunchKernelGGL((copy_rows_pow2_kernel<KIND, SCATTER>), dim3((unsigned)blocks), dim3(256), 0, st, c, lg);
+    return hipGetLastError();
+  }
+  if constexpr (SCATTER) return hipErrorInvalidValue;  // scatter walks exist only for the 16-byte path
+  long long blocks = (nrows + 3) / 4;
   if (blocks > 4096) blocks = 4096;
   const dim3 grid((unsigned)blocks), block(256);
   if (al % 16 == 0) {
@@ -337,6 +394,12 @@ hipError_t launch_ulysses(const void* in, void* out, int n, int64_t s_local, int
                           hipStream_t st) {
   const long long runs = (long long)n * n * s_local;
   if (inverse) return launch_copy<MAP_ULY_INV>(in, out, runs, run_bytes, (int)s_local, n, 0, st);
+  // forward: walking the source in order (sequential reads, n write streams) and
+  // scattering with the inverse map beats gathering 2 KB runs at an n-run stride
+  const uintptr_t al = (uintptr_t)in | (uintptr_t)out | (uintptr_t)run_bytes;
+  const long long cpr16 = run_bytes / 16;
+  if (al % 16 == 0 && cpr16 <= 1024 && (cpr16 & (cpr16 - 1)) == 0)
+    return launch_copy<MAP_ULY_INV, true>(in, out, runs, run_bytes, (int)s_local, n, 0, st);
   return launch_copy<MAP_ULY_FWD>(in, out, runs, run_bytes, (int)s_local, n, 0, st);
 }
 
