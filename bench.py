@@ -205,10 +205,10 @@ def main():
         ra.cp_reorder(q_g, cp, w.partition, out=q_p)
         ra.cp_reorder(k_g, cp, w.partition, out=k_p)
         ra.cp_reorder(v_g, cp, w.partition, out=v_p)
-        for _ in range(12):
+        for _ in range(24):
             ra.ra_forward_planned(q_p[rank], k_p, v_p, plan, out=out, lse=lse)
         torch.cuda.synchronize()
-        print(json.dumps({"mode": "attn-only", "launches": 12, "flops_per_launch": flops}))
+        print(json.dumps({"mode": "attn-only", "launches": 24, "flops_per_launch": flops}))
         return
 
     def step():
