@@ -82,7 +82,10 @@ def test_forward_validation_codes():
     need = ra.ra_workspace_size(sh, 4, 0)
     assert need > 0
     assert fwd(sh, ws=None) == ra.RA_ERR_WORKSPACE
-    assert fwd(sh, ws_bytes=need - 1) == ra.RA_ERR_WORKSPACE
+    assert fwd(sh, ws_bytes=256) == ra.RA_ERR_WORKSPACE
+    # ra_workspace_size covers both the merged and the per-step layouts; the per-step one is larger here
+    assert _lib().ra_forward_steps(P, P, P, None, 0, 4, 0, 1, ctypes.byref(sh), P, P, P, need - 1, None) \
+        == ra.RA_ERR_WORKSPACE
 
 
 def test_cu_seqlens_validation():
