@@ -34,10 +34,12 @@ from .attention import (attention_rows, attention_rank, step_partials, lse_merge
                         online_softmax_blocks, ring_chunk_order)
 from .layouts import cp_reorder, ulysses_permute
 from .classify import classify_tiles, SKIP, PARTIAL, FULL
+from .backward import attention_rows_backward, attention_rank_backward, ring_step_gradients
 
 __all__ = [
     "positions", "doc_bounds", "visible_matrix", "visible_counts",
     "attention_rows", "attention_rank", "step_partials", "lse_merge", "merge_steps",
     "online_softmax_blocks", "ring_chunk_order",
     "cp_reorder", "ulysses_permute", "classify_tiles", "SKIP", "PARTIAL", "FULL",
+    "attention_rows_backward", "attention_rank_backward", "ring_step_gradients",
 ]
