@@ -149,6 +149,37 @@ ra_status ra_forward_steps(const void* q, const void* k, const void* v, const in
                            const ra_shape* shape, float* o_steps, float* lse_steps, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* Bytes of device workspace that ra_backward needs for this shape, CP size and
+ * document count (both kernels' work lists and the per-row sums dO . O).
+ * Returns 0 for an invalid shape. */
+size_t ra_backward_workspace_size(const ra_shape* shape, int32_t cp_size, int32_t n_docs);
+
+/* Gradients of one rank's ring attention. The pages train with these layers
+ * ([How-to] 4: a forward and a backward per step; [CP-TE] 4: training
+ * throughput) but give no backward equations; this is the chain rule of the
+ * forward's definition, with P = exp(s - LSE) the probabilities over all ring
+ * steps and dO the gradient of the loss with respect to out:
+ *   dV_k = sum_i P_ik dO_i;  dP_ik = dO_i . v_k;  dS_ik = P_ik (dP_ik - dO_i . O_i)
+ *   dQ_i = scale sum_k dS_ik k_k;  dK_k = scale sum_i dS_ik q_i
+ * (GQA: dK / dV of a KV head sum over the query heads that read it.)
+ *   q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape: as in ra_forward
+ *   out        device [S_l][hq][d] out_dtype: the forward output
+ *   lse        device fp32 [hq][S_l]: the forward LSE (natural log, all steps merged)
+ *   dout       device [S_l][hq][d] in_dtype: gradient with respect to out
+ *   dq         device fp32 [S_l][hq][d]: gradient with respect to this rank's q
+ *   dk, dv     device fp32 [cp][S_l][hkv][d]: this rank's contribution to the
+ *              gradient of every chunk's k and v, chunk s at index s in its owner's
+ *              partition-local order (the partial of ring step (rank - s) mod cp;
+ *              a real ring adds the ranks' partials as the chunk travels, so the
+ *              sum over ranks is the gradient of the whole sequence). Chunks and
+ *              keys that no row of the rank sees are written as 0.
+ *   workspace  device scratch of at least ra_backward_workspace_size() bytes
+ * Rows whose LSE is -inf contribute nothing. Deterministic: no atomics. */
+ra_status ra_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                      const void* dout, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size,
+                      int32_t rank, int32_t partition, const ra_shape* shape, float* dq, float* dk, float* dv,
+                      void* workspace, size_t ws_bytes, void* stream);
+
 /* fp32 LSE merge of two normalised partials (derived from the online-softmax
  * update of [SP-concept] 二 at chunk granularity):
  *   LSE = ln(e^lse_a + e^lse_b);  O = e^(lse_a - LSE) o_a + e^(lse_b - LSE) o_b

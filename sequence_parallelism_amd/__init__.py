@@ -4,8 +4,9 @@ Argument marshalling only: every step of the path runs in the HIP kernels of
 libra.so. PyTorch provides device memory and the current stream. The binding
 fails loudly when the library is missing; there is no fallback of any kind.
 
-Function names mirror the C entry points: ra_forward, ra_forward_steps,
-ra_lse_merge, ra_classify, ulysses_permute, cp_reorder, ra_workspace_size,
+Function names mirror the C entry points: ra_forward, ra_plan,
+ra_forward_planned, ra_forward_steps, ra_backward, ra_lse_merge, ra_classify,
+ulysses_permute, cp_reorder, ra_workspace_size, ra_backward_workspace_size,
 ra_status_string.
 """
 from __future__ import annotations
@@ -27,7 +28,8 @@ RA_BF16, RA_F32 = 0, 1
 PARTITIONS = {"contiguous": 0, "zigzag": 1, "striped": 2}
 
 # Symbols declared in include/ra.h.
-EXPORTS = ("ra_workspace_size", "ra_forward", "ra_plan", "ra_forward_planned", "ra_forward_steps", "ra_lse_merge", "ra_classify",
+EXPORTS = ("ra_workspace_size", "ra_forward", "ra_plan", "ra_forward_planned", "ra_forward_steps",
+           "ra_backward_workspace_size", "ra_backward", "ra_lse_merge", "ra_classify",
            "ulysses_permute", "cp_reorder", "ra_status_string", "ra_abi_version")
 
 
@@ -67,6 +69,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_forward_planned.restype = ctypes.c_int
     lib.ra_forward_steps.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
     lib.ra_forward_steps.restype = ctypes.c_int
+    lib.ra_backward_workspace_size.argtypes = [shp, i32, i32]
+    lib.ra_backward_workspace_size.restype = sz
+    lib.ra_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, vp, sz, vp]
+    lib.ra_backward.restype = ctypes.c_int
     lib.ra_lse_merge.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.ra_lse_merge.restype = ctypes.c_int
     lib.ra_classify.argtypes = [shp, vp, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]
@@ -237,6 +243,43 @@ def ra_forward_steps(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, 
                                          _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "ra_forward_steps")
     return o_steps, lse_steps
+
+
+def ra_backward_workspace_size(shape: ra_shape, cp_size: int, n_docs: int = 0) -> int:
+    return int(load_library().ra_backward_workspace_size(ctypes.byref(shape), int(cp_size), int(n_docs)))
+
+
+def ra_backward(q, k, v, out, lse, dout, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partition="contiguous",
+                *, causal: bool = True, softmax_scale: float = 0.0, dq=None, dk=None, dv=None, workspace=None,
+                stream=None):
+    """Gradients of one rank's ring attention. q, dout [S_l,hq,d] (input dtype); k, v
+    [cp,S_l,hkv,d]; out [S_l,hq,d] and lse fp32 [hq,S_l] from the forward. Returns
+    (dq fp32 [S_l,hq,d], dk fp32 [cp,S_l,hkv,d], dv fp32 [cp,S_l,hkv,d]): dk / dv hold
+    this rank's contribution to every chunk's gradient."""
+    import torch
+    shape, s_l, hq, d, _ = _attn_common(q, k, v, cp_size, causal, softmax_scale, out.dtype)
+    if dout.shape != q.shape or dout.dtype != q.dtype or out.shape != q.shape or lse.shape != (hq, s_l):
+        raise ValueError("out / dout must be [S_l,hq,d] (dout in q's dtype), lse [hq,S_l]")
+    for t in (out, lse, dout):
+        if not t.is_contiguous():
+            raise ValueError("out, lse, dout must be contiguous")
+    cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
+    hkv = k.shape[2]
+    if dq is None:
+        dq = torch.empty((s_l, hq, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((cp_size, s_l, hkv, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((cp_size, s_l, hkv, d), dtype=torch.float32, device=q.device)
+    need = ra_backward_workspace_size(shape, cp_size, n_docs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().ra_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), cu_ptr, n_docs,
+                                    int(cp_size), int(rank), _part(partition), ctypes.byref(shape), _ptr(dq),
+                                    _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "ra_backward")
+    return dq, dk, dv
 
 
 def ra_lse_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):

@@ -65,6 +65,61 @@ ra_status run_attention(const void* q, const void* k, const void* v, int32_t nd,
   return e == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
+ra_status run_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition,
+                       const ra_shape* shape, float* dq, float* dk, float* dv, void* workspace, hipStream_t st) {
+  const BwdLayout B = bwd_layout(shape, cp, nd);
+  const Layout& L = B.fwd;
+  char* ws = (char*)workspace;
+  const ra_status p = run_plan(cu, nd, cp, rank, partition, shape, workspace, st);
+  if (p != RA_OK) return p;
+  const int* dcu = nd > 1 ? (const int*)(ws + L.cu_off) : nullptr;
+  if (launch_kv_worklist(dcu, nd, (int)shape->s_total, L.s_local, cp, rank, partition, shape->causal, B.bq, B.bk,
+                         B.nqt_kv, B.nkt_kv, B.kwl_stride, (int*)(ws + B.kwl_off), (int*)(ws + B.kcount_off),
+                         (int*)(ws + B.korder_off), st) != hipSuccess)
+    return RA_ERR_HIP;
+  float* dsum = (float*)(ws + B.dsum_off);
+  if (launch_bwd_dsum(out, dout, dsum, L.s_local, shape->hq, shape->d, shape->out_dtype == RA_BF16,
+                      shape->in_dtype == RA_BF16, st) != hipSuccess)
+    return RA_ERR_HIP;
+  const float scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.f / sqrtf((float)shape->d);
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dsum = dsum;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.cu = dcu;
+  a.wl = (const int*)(ws + L.wl_off);
+  a.wl_count = (const int*)(ws + L.count_off);
+  a.order = (const int*)(ws + L.order_off);
+  a.kwl = (const int*)(ws + B.kwl_off);
+  a.kwl_count = (const int*)(ws + B.kcount_off);
+  a.korder = (const int*)(ws + B.korder_off);
+  a.n_docs = nd;
+  a.s_total = (int)shape->s_total;
+  a.s_local = L.s_local;
+  a.cp = cp;
+  a.rank = rank;
+  a.part = partition;
+  a.causal = shape->causal;
+  a.hq = shape->hq;
+  a.hkv = shape->hkv;
+  a.nqt = L.nqt;
+  a.nkt = L.nkt;
+  a.wl_stride = L.wl_stride;
+  a.nkt_kv = B.nkt_kv;
+  a.nqt_kv = B.nqt_kv;
+  a.kwl_stride = B.kwl_stride;
+  a.scale = scale;
+  a.scale_log2 = scale * kLog2e;
+  return launch_ring_bwd(a, shape->d, shape->in_dtype == RA_BF16, st) == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,6 +193,25 @@ ra_status ra_forward_steps(const void* q, const void* k, const void* v, const in
   if (p != RA_OK) return p;
   return run_attention(q, k, v, nd, cp_size, rank, partition, shape, nullptr, nullptr, o_steps, lse_steps, workspace,
                        st, true);
+}
+
+size_t ra_backward_workspace_size(const ra_shape* shape, int32_t cp_size, int32_t n_docs) {
+  if (!shape || shape->s_total < 1 || shape->s_total > ((int64_t)1 << 30)) return 0;
+  if (cp_size < 1 || cp_size > 64 || shape->s_total % cp_size) return 0;
+  if (shape->in_dtype != RA_BF16 && shape->in_dtype != RA_F32) return 0;
+  if (shape->hq < 1 || shape->hq > 4096) return 0;
+  return bwd_layout(shape, cp_size, n_docs > 1 ? n_docs : 1).total;
+}
+
+ra_status ra_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                      const void* dout, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size, int32_t rank,
+                      int32_t partition, const ra_shape* shape, float* dq, float* dk, float* dv, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  const ra_status s = check_backward(q, k, v, out, lse, dout, cu_seqlens, n_docs, cp_size, rank, partition, shape, dq,
+                                     dk, dv, workspace, ws_bytes);
+  if (s != RA_OK) return s;
+  return run_backward(q, k, v, out, lse, dout, cu_seqlens, effective_docs(cu_seqlens, n_docs), cp_size, rank,
+                      partition, shape, dq, dk, dv, workspace, as_stream(stream));
 }
 
 ra_status ra_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, const float* lse_a, const float* o_b,

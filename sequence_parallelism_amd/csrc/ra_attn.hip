@@ -29,81 +29,10 @@
 // is never transposed in memory. exp is exp2 with softmax_scale*log2(e)
 // folded into one FMA (e^x = 2^(x log2 e)).
 #include "ra_common.h"
+#include "ra_device.h"
 #include "ra_internal.h"
 
 namespace ra {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ float swap_half_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float swap_half_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)((__attribute__((address_space(3))) char*)p));
-}
-
-// Query head served by block-slot hs: blocks hs, hs+8, ... share an XCD, so a
-// contiguous run of hq/8 heads (one KV head under 4:1 GQA) lands on one XCD.
-__device__ __forceinline__ int head_of_slot(int hs, int hq) {
-  return (hq % 8 == 0) ? (hs % 8) * (hq / 8) + hs / 8 : hs;
-}
-
-// Chunk owner visited at ring step t (any t >= 0).
-__device__ __forceinline__ int ring_owner(int rank, int t, int cp) { return ((rank - t) % cp + cp) % cp; }
-
-// Work-list length of a tile, clamped to the reserved stride.
-__device__ __forceinline__ int clamp_count(int n, int stride) { return n < 0 ? 0 : (n > stride ? stride : n); }
-
-// Per-lane visible tile-local key indices: [i0a, i0a + la) U [i0b, i0b + lb).
-struct TileMask {
-  int i0a, la, i0b, lb;
-};
-
-__device__ __forceinline__ TileMask tile_mask(const PartInfo& p, int owner, int ka, int kb, int cls, bool row_ok,
-                                              int lo, int hi) {
-  TileMask t{0, 0, 0, 0};
-  if (!row_ok) return t;
-  if (cls == CLS_FULL) {
-    t.la = kb - ka;
-    return t;
-  }
-  Run kr[2];
-  const int nr = runs_of(p, owner, ka, kb, kr);
-  int n0, n1;
-  if (nr > 0) {
-    run_range(kr[0], lo, hi, n0, n1);
-    t.i0a = kr[0].off + n0;
-    t.la = n1 >= n0 ? n1 - n0 + 1 : 0;
-  }
-  if (nr > 1) {
-    run_range(kr[1], lo, hi, n0, n1);
-    t.i0b = kr[1].off + n0;
-    t.lb = n1 >= n0 ? n1 - n0 + 1 : 0;
-  }
-  return t;
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
-}
 
 // The accumulator is rescaled only when a row's running max must grow by more
 // than this (log2 units): until then the stale max is kept, so P <= 2^8, which

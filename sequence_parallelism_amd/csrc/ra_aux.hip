@@ -108,7 +108,12 @@ hipError_t launch_worklist(const int* cu, int n_docs, int s_total, int s_local, 
   hipLaunchKernelGGL(worklist_kernel, dim3(nqt), dim3(256), 0, st, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, wl_count, nqt, order);
+  return launch_order(wl_count, nqt, order, st);
+}
+
+hipError_t launch_order(const int* count, int n, int* order, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, st, count, n, order);
   return hipGetLastError();
 }
 

@@ -1,0 +1,829 @@
+// Backward of the ring-step attention for gfx950 (CDNA4).
+//
+// The pages train with these layers (forward and backward of every step) but
+// print no backward equations; the kernels compute the chain rule of the
+// forward's definition. With P_ik = exp(s_ik - LSE_i) the probabilities of the
+// whole ring (LSE from the forward, so nothing is renormalised per step) and
+// dO the gradient of the rank's output rows:
+//     D_i   = sum_c dO_ic O_ic                 (= sum_k P_ik dP_ik)
+//     dP_ik = dO_i . v_k,   dS_ik = P_ik (dP_ik - D_i)
+//     dQ_i  = scale sum_k dS_ik k_k
+//     dK_k  = scale sum_i dS_ik q_i,   dV_k = sum_i P_ik dO_i
+// P is recomputed from Q, K and the stored LSE instead of being kept from the
+// forward (the recompute-for-memory trade that the Sequence Parallelism
+// concept page names for activations).
+//
+// Two kernels, no atomics (results are bit-reproducible):
+//  * dQ, query-tile parallel, over the forward's work list (same tiles): the
+//    transposed forward, S^T = K Q^T and dP^T = V dO^T (K and V rows from
+//    LDS, Q and dO of the lane's row in registers), then dQ^T += K^T dS^T with
+//    K^T from the transposing LDS read.
+//  * dK and dV, key-tile parallel: a workgroup owns 128 keys of one chunk and
+//    one KV head, each wave 32 keys with K and V in registers, and walks the
+//    query tiles (64 rows) that see them, for every query head of the GQA
+//    group: X = Q K^T and dP = dO V^T (Q and dO rows from LDS), then
+//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from the transposing
+//    read. One ring step's contribution to a chunk is exactly that chunk's
+//    key tiles, so dK / dV of chunk s are this rank's step-(rank - s) partials.
+// Both MFMA kernels keep the lane <-> (query row or key) ownership of the
+// forward: every softmax-side quantity is a per-lane scalar or a 16-wide
+// per-lane vector, and P / dS become the next MFMA's B operand in place.
+#include "ra_common.h"
+#include "ra_device.h"
+#include "ra_internal.h"
+
+namespace ra {
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO_ic O_ic per (row, head): d/8 lanes per pair, 8 elements each.
+// ---------------------------------------------------------------------------
+template <bool OUT_BF16, bool IN_BF16>
+__global__ void __launch_bounds__(256) bwd_dsum_kernel(const void* out, const void* dout, float* dsum, int rows,
+                                                       int hq, int d) {
+  const int per = d >> 3;  // 8 or 16 lanes, a power of two dividing 64
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long pair = gid / per;
+  const int sub = (int)(gid - pair * per);
+  float acc = 0.f;
+  const bool ok = pair < (long long)rows * hq;
+  if (ok) {
+    const size_t off = (size_t)pair * d + 8 * sub;
+    float o[8], g[8];
+    if constexpr (OUT_BF16) {
+      const bf16x8 x = *(const bf16x8*)((const __bf16*)out + off);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = (float)x[i];
+    } else {
+      const f32x4 x0 = *(const f32x4*)((const float*)out + off), x1 = *(const f32x4*)((const float*)out + off + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = x0[i], o[4 + i] = x1[i];
+    }
+    if constexpr (IN_BF16) {
+      const bf16x8 x = *(const bf16x8*)((const __bf16*)dout + off);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[i] = (float)x[i];
+    } else {
+      const f32x4 x0 = *(const f32x4*)((const float*)dout + off), x1 = *(const f32x4*)((const float*)dout + off + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[i] = x0[i], g[4 + i] = x1[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(o[i], g[i], acc);
+  }
+  for (int m = per >> 1; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (ok && sub == 0) {
+    const long long row = pair / hq;
+    const int h = (int)(pair - row * hq);
+    dsum[(size_t)h * rows + row] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ, bf16 inputs, MFMA path. Tiles, grid and work list of the forward kernel.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs a) {
+  constexpr int BM = kAttnBf16BM, BN = kAttnBf16BN;
+  static_assert(BM == 128 && BN == 64, "tile shape is baked into the lane mapping");
+  // head_dim 128: direct global->LDS tile loads into 256-byte rows, chunks
+  // placed by swz_rt (K is read row-wise and transposed, V row-wise);
+  // head_dim 64: register-staged tiles with 16-byte padded rows.
+  constexpr bool DMA = D == 128;
+  constexpr int ROW = DMA ? D : D + 8;
+  constexpr int TILE = BN * ROW, STAGE = 2 * TILE;
+  constexpr int CHUNKS = BN * D / 8, PER = CHUNKS / 256, CPR = D / 8;
+  constexpr int NCT = D / 32, NKD = D / 16;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi32 = lane >> 5, l32 = lane & 31;
+  const int qt = a.order[blockIdx.x / a.hq];
+  if (qt < 0 || qt >= a.nqt) return;
+  const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
+  const int g = h / (a.hq / a.hkv);
+  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const int row = qt * BM + wave * 32 + l32;
+  const bool row_ok = row < a.s_local;
+  const float C = a.scale_log2;
+
+  // B operands of S^T = K Q^T and dP^T = V dO^T: lane holds 8 elements of its row.
+  bf16x8 qreg[NKD], oreg[NKD];
+  {
+    const uint32_t bytes = (uint32_t)a.s_local * a.hq * D * 2u;
+    const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(a.q, bytes);
+    const __amdgpu_buffer_rsrc_t orr = buffer_rsrc(a.dout, bytes);
+    const uint32_t off = ((uint32_t)row * a.hq + h) * D * 2u + 16u * hi32;
+#pragma unroll
+    for (int j = 0; j < NKD; ++j) {
+      qreg[j] = __builtin_bit_cast(bf16x8, buffer_load16(qr, off + 32u * j));
+      oreg[j] = __builtin_bit_cast(bf16x8, buffer_load16(orr, off + 32u * j));
+    }
+  }
+  // Rows past the end, or with no visible key (LSE = -inf), get P = 0: exp2(x - inf).
+  float lse2 = INFINITY, dsum = 0.f;
+  int lo = 1, hi = 0;
+  if (row_ok) {
+    const float l = a.lse[(size_t)h * a.s_local + row];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    dsum = a.dsum[(size_t)h * a.s_local + row];
+    row_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, a.rank, row), lo, hi);
+  }
+
+  f32x16 acc[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
+
+  const uint32_t kv_row_bytes = (uint32_t)a.hkv * D * 2u;
+  const uint32_t chunk_bytes = (uint32_t)a.s_local * kv_row_bytes;
+  const int n_ent = clamp_count(a.wl_count[qt], a.wl_stride);
+  const int* list = a.wl + (size_t)qt * a.wl_stride;
+
+  // Direct loads: wave w fills rows 16 w .. 16 w + 15 of a tile, 4 rows per
+  // instruction; lane L lands in slot L % 16 of row L / 16 and fetches the
+  // logical chunk that swz_rt places there.
+  uint32_t d_off[4];
+  uint32_t goff[PER];
+  int slot[PER];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4), pc = lane & 15;
+      d_off[i] = (uint32_t)r * kv_row_bytes + ((uint32_t)g * D + 8 * (pc ^ swz_rt(r))) * 2u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / CPR, c8 = c % CPR;
+      goff[i] = (uint32_t)r * kv_row_bytes + ((uint32_t)g * D + c8 * 8) * 2u;
+      slot[i] = r * ROW + c8 * 8;
+    }
+  }
+  uint4 rk[DMA ? 1 : PER], rv[DMA ? 1 : PER];
+  auto load_tile = [&](int ent, int buf) {
+    const int t = wl_step(ent), J = wl_tile(ent);
+    const size_t cbase = (size_t)ring_owner(a.rank, t, a.cp) * chunk_bytes;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc((const char*)a.k + cbase, chunk_bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc((const char*)a.v + cbase, chunk_bytes);
+    const uint32_t toff = (uint32_t)J * BN * kv_row_bytes;
+    if constexpr (DMA) {
+      __attribute__((address_space(3))) char* kl =
+          (__attribute__((address_space(3))) char*)(smem + buf * STAGE) + 4096 * wave;
+      __attribute__((address_space(3))) char* vl = kl + TILE * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16,
+                                                 (int)(toff + d_off[i]), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16,
+                                                 (int)(toff + d_off[i]), 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        rk[i] = buffer_load16(kr, toff + goff[i]);
+        rv[i] = buffer_load16(vr, toff + goff[i]);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if constexpr (DMA) {
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      __bf16* ks = smem + buf * STAGE;
+      __bf16* vs = ks + TILE;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        *(uint4*)(ks + slot[i]) = rk[i];
+        *(uint4*)(vs + slot[i]) = rv[i];
+      }
+    }
+  };
+
+  if (n_ent > 0) {
+    load_tile(list[0], 0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int e = 0; e < n_ent; ++e) {
+    const int ent = list[e];
+    const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
+    const bool ent_ok = t < a.cp && J < a.nkt && cls != CLS_SKIP;
+    if (e + 1 < n_ent) load_tile(list[e + 1], (e + 1) & 1);
+
+    const int ka = J * BN;
+    const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
+    bool need_mask = kb - ka < BN || cls == CLS_PARTIAL;
+    bool do_tile = ent_ok;
+    TileMask tm{0, BN, 0, 0};
+    if (do_tile && need_mask) {
+      tm = tile_mask(pinfo, ring_owner(a.rank, t, a.cp), ka, kb, cls, row_ok, lo, hi);
+      do_tile = __any(tm.la > 0 || tm.lb > 0);
+      need_mask = !__all((tm.i0a == 0 && tm.la == BN) || !row_ok);
+    }
+
+    if (do_tile) {
+      const __bf16* ks = smem + (e & 1) * STAGE;
+      const __bf16* vs = ks + TILE;
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int j = 0; j < NKD; ++j)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int kr = kt * 32 + l32, kc = 2 * j + hi32;
+          const int o = kr * ROW + 8 * (DMA ? (kc ^ swz_rt(kr)) : kc);
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ks + o), qreg[j], s[kt], 0, 0, 0);
+          dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vs + o), oreg[j], dp[kt], 0, 0, 0);
+        }
+      __builtin_amdgcn_s_setprio(0);
+      // lane holds keys n = 32 kt + 8 (i/4) + 4 hi32 + (i%4) of its row; dS^T in place of S^T
+      const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int n = kt * 32 + 8 * (i >> 2) + (i & 3);
+          const bool vis =
+              !need_mask || ((unsigned)(n + ba) < (unsigned)tm.la) | ((unsigned)(n + bb) < (unsigned)tm.lb);
+          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], C, -lse2)) : 0.f;
+          s[kt][i] = vis ? p * (dp[kt][i] - dsum) : 0.f;
+        }
+      // dQ^T += K^T dS^T
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 sb0 = __builtin_convertvector(s[kt].lo, bf16x8);
+        const bf16x8 sb1 = __builtin_convertvector(s[kt].hi, bf16x8);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int r0 = kt * 32 + jj * 16 + 4 * hi32 + ((lane & 15) >> 2);
+            const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            int o0 = r0 * ROW + c0, o1 = (r0 + 8) * ROW + c0;
+            if constexpr (DMA) {
+              o0 = r0 * ROW + ((((c0 >> 3) ^ swz_rt(r0)) << 3) | (c0 & 7));
+              o1 = (r0 + 8) * ROW + ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7));
+            }
+            const bf16x4 k0 = lds_read_tr(ks + o0);
+            const bf16x4 k1 = lds_read_tr(ks + o1);
+            const bf16x8 kk = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, jj ? sb1 : sb0, acc[c], 0, 0, 0);
+          }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+
+    if (e + 1 < n_ent) store_tile((e + 1) & 1);
+    __syncthreads();
+  }
+
+  if (row_ok) {
+    float* dq = a.dq + ((size_t)row * a.hq + h) * D;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = c * 32 + 8 * i4 + 4 * hi32;
+        *(f32x4*)(dq + col) = f32x4{acc[c][4 * i4], acc[c][4 * i4 + 1], acc[c][4 * i4 + 2], acc[c][4 * i4 + 3]} *
+                              a.scale;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV, bf16 inputs, MFMA path. Workgroup = (key tile of 128 keys of one
+// chunk, KV head); wave = 32 keys; query tiles of 64 rows.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs a) {
+  constexpr int BK = kBwdBf16BK, BQ = kBwdBf16BQ;
+  static_assert(BK == 128 && BQ == 64, "tile shape is baked into the lane mapping");
+  constexpr bool DMA = D == 128;
+  constexpr int ROW = DMA ? D : D + 8;
+  constexpr int TILE = BQ * ROW, STAGE = 2 * TILE;
+  constexpr int CHUNKS = BQ * D / 8, PER = CHUNKS / 256, CPR = D / 8;
+  constexpr int NCT = D / 32, NKD = D / 16;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][BQ];  // [buf][LSE * log2 e | D][row]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi32 = lane >> 5, l32 = lane & 31;
+  const int n_kt = a.cp * a.nkt_kv;
+  const int kt = a.korder[blockIdx.x / a.hkv];
+  if (kt < 0 || kt >= n_kt) return;
+  const int g = head_of_slot(blockIdx.x % a.hkv, a.hkv);
+  const int G = a.hq / a.hkv;
+  const int owner = kt / a.nkt_kv, J = kt - owner * a.nkt_kv;
+  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const int key = J * BK + wave * 32 + l32;
+  const bool key_ok = key < a.s_local;
+  const float C = a.scale_log2;
+
+  // B operands of X = Q K^T and dP = dO V^T: lane holds 8 elements of its key.
+  const uint32_t kv_row_bytes = (uint32_t)a.hkv * D * 2u;
+  const uint32_t chunk_bytes = (uint32_t)a.s_local * kv_row_bytes;
+  bf16x8 kreg[NKD], vreg[NKD];
+  {
+    const size_t cbase = (size_t)owner * chunk_bytes;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc((const char*)a.k + cbase, chunk_bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc((const char*)a.v + cbase, chunk_bytes);
+    const uint32_t off = (uint32_t)key * kv_row_bytes + (uint32_t)g * D * 2u + 16u * hi32;
+#pragma unroll
+    for (int j = 0; j < NKD; ++j) {
+      kreg[j] = __builtin_bit_cast(bf16x8, buffer_load16(kr, off + 32u * j));
+      vreg[j] = __builtin_bit_cast(bf16x8, buffer_load16(vr, off + 32u * j));
+    }
+  }
+  int plo = 1, phi = 0;  // visible query positions of this key
+  if (key_ok) key_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, owner, key), plo, phi);
+
+  f32x16 dk[NCT], dv[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) dk[c] = dv[c] = f32x16{};
+
+  const int n_ent = clamp_count(a.kwl_count[kt], a.kwl_stride);
+  const int* list = a.kwl + (size_t)kt * a.kwl_stride;
+  const int total = n_ent * G;
+  const uint32_t q_row_bytes = (uint32_t)a.hq * D * 2u;
+  const uint32_t q_bytes = (uint32_t)a.s_local * q_row_bytes;
+  const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(a.q, q_bytes);
+  const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(a.dout, q_bytes);
+
+  uint32_t d_off[4];
+  uint32_t goff[PER];
+  int slot[PER];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + (lane >> 4), pc = lane & 15;
+      d_off[i] = (uint32_t)r * q_row_bytes + 8u * (pc ^ swz_rt(r)) * 2u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = tid + i * 256;
+      const int r = c / CPR, c8 = c % CPR;
+      goff[i] = (uint32_t)r * q_row_bytes + c8 * 16u;
+      slot[i] = r * ROW + c8 * 8;
+    }
+  }
+  uint4 rq[DMA ? 1 : PER], ro[DMA ? 1 : PER];
+  float rl = INFINITY, rd = 0.f;  // wave 0: LSE * log2 e and D of row `lane` of the next tile
+  auto load_tile = [&](int it, int buf) {
+    const int hh = it / n_ent;
+    const int ent = list[it - hh * n_ent];
+    const int h = g * G + hh, I = wl_tile(ent);
+    const uint32_t toff = (uint32_t)I * BQ * q_row_bytes + (uint32_t)h * D * 2u;
+    if constexpr (DMA) {
+      __attribute__((address_space(3))) char* ql =
+          (__attribute__((address_space(3))) char*)(smem + buf * STAGE) + 4096 * wave;
+      __attribute__((address_space(3))) char* ol = ql + TILE * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (__attribute__((address_space(3))) void*)(ql + 1024 * i), 16,
+                                                 (int)(toff + d_off[i]), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (__attribute__((address_space(3))) void*)(ol + 1024 * i), 16,
+                                                 (int)(toff + d_off[i]), 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        rq[i] = buffer_load16(qrs, toff + goff[i]);
+        ro[i] = buffer_load16(ors, toff + goff[i]);
+      }
+    }
+    if (wave == 0) {
+      const int r = I * BQ + lane;
+      rl = INFINITY;
+      rd = 0.f;
+      if (r < a.s_local && I < a.nqt_kv) {
+        const float l = a.lse[(size_t)h * a.s_local + r];
+        rl = l == -INFINITY ? INFINITY : l * kLog2e;
+        rd = a.dsum[(size_t)h * a.s_local + r];
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    if constexpr (DMA) {
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      __bf16* qs = smem + buf * STAGE;
+      __bf16* os = qs + TILE;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        *(uint4*)(qs + slot[i]) = rq[i];
+        *(uint4*)(os + slot[i]) = ro[i];
+      }
+    }
+    if (wave == 0) {
+      rowv[buf][0][lane] = rl;
+      rowv[buf][1][lane] = rd;
+    }
+  };
+
+  if (total > 0) {
+    load_tile(0, 0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < total; ++it) {
+    const int ent = list[it % n_ent];
+    const int I = wl_tile(ent), cls = wl_cls(ent);
+    const bool ent_ok = I < a.nqt_kv && cls != CLS_SKIP;
+    if (it + 1 < total) load_tile(it + 1, (it + 1) & 1);
+
+    const int qa = I * BQ;
+    const int qb = qa + BQ < a.s_local ? qa + BQ : a.s_local;
+    bool need_mask = qb - qa < BQ || cls == CLS_PARTIAL;
+    bool do_tile = ent_ok;
+    TileMask tm{0, BQ, 0, 0};
+    if (do_tile && need_mask) {
+      tm = tile_mask(pinfo, a.rank, qa, qb, cls, key_ok, plo, phi);
+      do_tile = __any(tm.la > 0 || tm.lb > 0);
+      need_mask = !__all((tm.i0a == 0 && tm.la == BQ) || !key_ok);
+    }
+
+    if (do_tile) {
+      const int buf = it & 1;
+      const __bf16* qs = smem + buf * STAGE;
+      const __bf16* os = qs + TILE;
+      const float* l2s = rowv[buf][0];
+      const float* dss = rowv[buf][1];
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        f32x16 x = f32x16{}, dp = f32x16{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int j = 0; j < NKD; ++j) {
+          const int qr = qh * 32 + l32, kc = 2 * j + hi32;
+          const int o = qr * ROW + 8 * (DMA ? (kc ^ swz_rt(qr)) : kc);
+          x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qs + o), kreg[j], x, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(os + o), vreg[j], dp, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        // lane holds query rows n = 32 qh + 8 (i/4) + 4 hi32 + (i%4) of its key: P in x, dS in dp
+        const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int n0 = qh * 32 + 8 * i4 + 4 * hi32;
+          const f32x4 L = *(const f32x4*)(l2s + n0);
+          const f32x4 Dd = *(const f32x4*)(dss + n0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * i4 + u, n = qh * 32 + 8 * i4 + u;
+            const bool vis =
+                !need_mask || ((unsigned)(n + ba) < (unsigned)tm.la) | ((unsigned)(n + bb) < (unsigned)tm.lb);
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], C, -L[u])) : 0.f;
+            x[i] = p;
+            dp[i] = vis ? p * (dp[i] - Dd[u]) : 0.f;
+          }
+        }
+        const bf16x8 pb0 = __builtin_convertvector(x.lo, bf16x8), pb1 = __builtin_convertvector(x.hi, bf16x8);
+        const bf16x8 sb0 = __builtin_convertvector(dp.lo, bf16x8), sb1 = __builtin_convertvector(dp.hi, bf16x8);
+        // dV^T += dO^T P,  dK^T += Q^T dS
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int r0 = qh * 32 + jj * 16 + 4 * hi32 + ((lane & 15) >> 2);
+            const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            int o0 = r0 * ROW + c0, o1 = (r0 + 8) * ROW + c0;
+            if constexpr (DMA) {
+              o0 = r0 * ROW + ((((c0 >> 3) ^ swz_rt(r0)) << 3) | (c0 & 7));
+              o1 = (r0 + 8) * ROW + ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7));
+            }
+            const bf16x8 ot = __builtin_shufflevector(lds_read_tr(os + o0), lds_read_tr(os + o1), 0, 1, 2, 3, 4, 5, 6,
+                                                      7);
+            const bf16x8 qt8 = __builtin_shufflevector(lds_read_tr(qs + o0), lds_read_tr(qs + o1), 0, 1, 2, 3, 4, 5,
+                                                       6, 7);
+            dv[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, jj ? pb1 : pb0, dv[c], 0, 0, 0);
+            dk[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt8, jj ? sb1 : sb0, dk[c], 0, 0, 0);
+          }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+
+    if (it + 1 < total) store_tile((it + 1) & 1);
+    __syncthreads();
+  }
+
+  if (key_ok) {
+    const size_t base = (((size_t)owner * a.s_local + key) * a.hkv + g) * D;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = c * 32 + 8 * i4 + 4 * hi32;
+        *(f32x4*)(a.dk + base + col) =
+            f32x4{dk[c][4 * i4], dk[c][4 * i4 + 1], dk[c][4 * i4 + 2], dk[c][4 * i4 + 3]} * a.scale;
+        *(f32x4*)(a.dv + base + col) = f32x4{dv[c][4 * i4], dv[c][4 * i4 + 1], dv[c][4 * i4 + 2], dv[c][4 * i4 + 3]};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs, VALU path. dQ: one wave, one query row per lane, the forward's
+// fp32 work list (key tiles of 32 staged in LDS).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(64) ring_bwd_dq_f32_kernel(const BwdArgs a) {
+  constexpr int BM = kAttnF32BM, BN = kAttnF32BN;
+  static_assert(BM == 64, "one query row per lane");
+  __shared__ float qs[BM][D + 1];
+  __shared__ float gs[BM][D + 1];
+  __shared__ __attribute__((aligned(16))) float ks[BN][D];
+  __shared__ __attribute__((aligned(16))) float vs[BN][D];
+
+  const int lane = threadIdx.x;
+  const int qt = a.order[blockIdx.x / a.hq];
+  if (qt < 0 || qt >= a.nqt) return;
+  const int h = blockIdx.x % a.hq;
+  const int g = h / (a.hq / a.hkv);
+  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const int row = qt * BM + lane;
+  const bool row_ok = row < a.s_local;
+  const float C = a.scale_log2;
+  {
+    const float* qp = (const float*)a.q + ((size_t)row * a.hq + h) * D;
+    const float* gp = (const float*)a.dout + ((size_t)row * a.hq + h) * D;
+    for (int c = 0; c < D; ++c) {
+      qs[lane][c] = row_ok ? qp[c] : 0.f;
+      gs[lane][c] = row_ok ? gp[c] : 0.f;
+    }
+  }
+  float lse2 = INFINITY, dsum = 0.f;
+  int lo = 1, hi = 0;
+  if (row_ok) {
+    const float l = a.lse[(size_t)h * a.s_local + row];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    dsum = a.dsum[(size_t)h * a.s_local + row];
+    row_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, a.rank, row), lo, hi);
+  }
+  float acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) acc[c] = 0.f;
+  const size_t kv_row = (size_t)a.hkv * D;
+  const size_t kv_chunk = (size_t)a.s_local * kv_row;
+  const int n_ent = clamp_count(a.wl_count[qt], a.wl_stride);
+  const int* list = a.wl + (size_t)qt * a.wl_stride;
+
+  for (int e = 0; e < n_ent; ++e) {
+    const int ent = list[e];
+    const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
+    if (t >= a.cp || J >= a.nkt || cls == CLS_SKIP) continue;  // uniform across the block
+    const int owner = ring_owner(a.rank, t, a.cp);
+    __syncthreads();
+    {
+      const float* kb = (const float*)a.k + owner * kv_chunk + (size_t)g * D;
+      const float* vb = (const float*)a.v + owner * kv_chunk + (size_t)g * D;
+      for (int idx = lane; idx < BN * D / 4; idx += 64) {
+        const int r = idx / (D / 4), c4 = idx % (D / 4);
+        const int j = J * BN + r;
+        f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+        if (j < a.s_local) {
+          kv = *(const f32x4*)(kb + (size_t)j * kv_row + 4 * c4);
+          vv = *(const f32x4*)(vb + (size_t)j * kv_row + 4 * c4);
+        }
+        *(f32x4*)&ks[r][4 * c4] = kv;
+        *(f32x4*)&vs[r][4 * c4] = vv;
+      }
+    }
+    __syncthreads();
+    const int ka = J * BN;
+    const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
+    const TileMask tm = tile_mask(pinfo, owner, ka, kb, cls, row_ok, lo, hi);
+    for (int j = 0; j < BN; ++j) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        s = __builtin_fmaf(qs[lane][c], ks[j][c], s);
+        dp = __builtin_fmaf(gs[lane][c], vs[j][c], dp);
+      }
+      const bool vis = ((unsigned)(j - tm.i0a) < (unsigned)tm.la) | ((unsigned)(j - tm.i0b) < (unsigned)tm.lb);
+      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s, C, -lse2)) : 0.f;
+      const float ds = p * (dp - dsum);
+#pragma unroll
+      for (int c = 0; c < D; ++c) acc[c] = __builtin_fmaf(ds, ks[j][c], acc[c]);
+    }
+  }
+  if (row_ok) {
+    float* dq = a.dq + ((size_t)row * a.hq + h) * D;
+    for (int c = 0; c < D; ++c) dq[c] = acc[c] * a.scale;
+  }
+}
+
+// dK and dV, fp32 VALU path: one wave, one key per lane (64 keys of one chunk
+// and one KV head), query tiles of 32 rows staged in LDS.
+template <int D>
+__global__ void __launch_bounds__(64) ring_bwd_dkv_f32_kernel(const BwdArgs a) {
+  constexpr int BK = kBwdF32BK, BQ = kBwdF32BQ;
+  static_assert(BK == 64, "one key per lane");
+  __shared__ float ks[BK][D + 1];
+  __shared__ float vs[BK][D + 1];
+  __shared__ __attribute__((aligned(16))) float qs[BQ][D];
+  __shared__ __attribute__((aligned(16))) float gs[BQ][D];
+  __shared__ float l2s[BQ], dss[BQ];
+
+  const int lane = threadIdx.x;
+  const int n_kt = a.cp * a.nkt_kv;
+  const int kt = a.korder[blockIdx.x / a.hkv];
+  if (kt < 0 || kt >= n_kt) return;
+  const int g = blockIdx.x % a.hkv;
+  const int G = a.hq / a.hkv;
+  const int owner = kt / a.nkt_kv, J = kt - owner * a.nkt_kv;
+  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const int key = J * BK + lane;
+  const bool key_ok = key < a.s_local;
+  const float C = a.scale_log2;
+  const size_t kv_row = (size_t)a.hkv * D;
+  {
+    const float* kp = (const float*)a.k + ((size_t)owner * a.s_local + key) * kv_row + (size_t)g * D;
+    const float* vp = (const float*)a.v + ((size_t)owner * a.s_local + key) * kv_row + (size_t)g * D;
+    for (int c = 0; c < D; ++c) {
+      ks[lane][c] = key_ok ? kp[c] : 0.f;
+      vs[lane][c] = key_ok ? vp[c] : 0.f;
+    }
+  }
+  int plo = 1, phi = 0;
+  if (key_ok) key_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, owner, key), plo, phi);
+  float dk[D], dv[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) dk[c] = dv[c] = 0.f;
+  const int n_ent = clamp_count(a.kwl_count[kt], a.kwl_stride);
+  const int* list = a.kwl + (size_t)kt * a.kwl_stride;
+  const size_t q_row = (size_t)a.hq * D;
+
+  for (int it = 0; it < n_ent * G; ++it) {
+    const int hh = it / n_ent;
+    const int ent = list[it - hh * n_ent];
+    const int I = wl_tile(ent), cls = wl_cls(ent);
+    if (I >= a.nqt_kv || cls == CLS_SKIP) continue;  // uniform across the block
+    const int h = g * G + hh;
+    __syncthreads();
+    for (int idx = lane; idx < BQ * D / 4; idx += 64) {
+      const int r = idx / (D / 4), c4 = idx % (D / 4);
+      const int i = I * BQ + r;
+      f32x4 qv = {0.f, 0.f, 0.f, 0.f}, gv = {0.f, 0.f, 0.f, 0.f};
+      if (i < a.s_local) {
+        qv = *(const f32x4*)((const float*)a.q + (size_t)i * q_row + (size_t)h * D + 4 * c4);
+        gv = *(const f32x4*)((const float*)a.dout + (size_t)i * q_row + (size_t)h * D + 4 * c4);
+      }
+      *(f32x4*)&qs[r][4 * c4] = qv;
+      *(f32x4*)&gs[r][4 * c4] = gv;
+    }
+    if (lane < BQ) {
+      const int i = I * BQ + lane;
+      float l2 = INFINITY, ds = 0.f;
+      if (i < a.s_local) {
+        const float l = a.lse[(size_t)h * a.s_local + i];
+        l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+        ds = a.dsum[(size_t)h * a.s_local + i];
+      }
+      l2s[lane] = l2;
+      dss[lane] = ds;
+    }
+    __syncthreads();
+    const int qa = I * BQ;
+    const int qb = qa + BQ < a.s_local ? qa + BQ : a.s_local;
+    const TileMask tm = tile_mask(pinfo, a.rank, qa, qb, cls, key_ok, plo, phi);
+    for (int r = 0; r < BQ; ++r) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        s = __builtin_fmaf(qs[r][c], ks[lane][c], s);
+        dp = __builtin_fmaf(gs[r][c], vs[lane][c], dp);
+      }
+      const bool vis = ((unsigned)(r - tm.i0a) < (unsigned)tm.la) | ((unsigned)(r - tm.i0b) < (unsigned)tm.lb);
+      const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s, C, -l2s[r])) : 0.f;
+      const float ds = p * (dp - dss[r]);
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        dk[c] = __builtin_fmaf(ds, qs[r][c], dk[c]);
+        dv[c] = __builtin_fmaf(p, gs[r][c], dv[c]);
+      }
+    }
+  }
+  if (key_ok) {
+    const size_t base = ((size_t)owner * a.s_local + key) * kv_row + (size_t)g * D;
+    for (int c = 0; c < D; ++c) {
+      a.dk[base + c] = dk[c] * a.scale;
+      a.dv[base + c] = dv[c];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key-side work list: for key tile kt = (chunk s, tile J), every query tile of
+// the rank whose class against it is not SKIP, packed with its class.
+// ---------------------------------------------------------------------------
+struct KvWlArgs {
+  const int* cu;
+  int n_docs, s_total, s_local, cp, rank, part, causal, bq, bk, nqt, nkt, stride;
+  int* wl;
+  int* count;
+};
+
+__global__ void __launch_bounds__(256) kv_worklist_kernel(const KvWlArgs w) {
+  __shared__ int wave_tot[4];
+  const int kt = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const PartInfo p{w.part, w.s_local, w.cp};
+  const int owner = kt / w.nkt, J = kt - owner * w.nkt;
+  const int ka = J * w.bk;
+  const int kb = ka + w.bk < w.s_local ? ka + w.bk : w.s_local;
+  int* out = w.wl + (size_t)kt * w.stride;
+  int base = 0;
+  for (int i0 = 0; i0 < w.nqt; i0 += 256) {
+    const int I = i0 + tid;
+    int c = CLS_SKIP;
+    if (I < w.nqt) {
+      const int qa = I * w.bq;
+      const int qb = qa + w.bq < w.s_local ? qa + w.bq : w.s_local;
+      c = classify_tile(p, w.rank, qa, qb, owner, ka, kb, w.cu, w.n_docs, w.s_total, w.causal);
+    }
+    const unsigned long long bal = __ballot(c != CLS_SKIP);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      before += i < wave ? wave_tot[i] : 0;
+      tot += wave_tot[i];
+    }
+    if (c != CLS_SKIP) out[base + before + below] = wl_pack(0, I, c);
+    base += tot;
+    __syncthreads();
+  }
+  if (tid == 0) w.count[kt] = base;
+}
+
+hipError_t launch_kv_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
+                              int causal, int bq, int bk, int nqt, int nkt, int stride, int* wl, int* count,
+                              int* order, hipStream_t st) {
+  const int n = cp * nkt;
+  if (n == 0) return hipSuccess;
+  KvWlArgs w{cu, n_docs, s_total, s_local, cp, rank, part, causal, bq, bk, nqt, nkt, stride, wl, count};
+  hipLaunchKernelGGL(kv_worklist_kernel, dim3(n), dim3(256), 0, st, w);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_order(count, n, order, st);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_bwd_dsum(const void* out, const void* dout, float* dsum, int rows, int hq, int d, int out_bf16,
+                           int in_bf16, hipStream_t st) {
+  const long long threads = (long long)rows * hq * (d / 8);
+  if (threads == 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (out_bf16 && in_bf16) {
+    hipLaunchKernelGGL((bwd_dsum_kernel<true, true>), grid, dim3(256), 0, st, out, dout, dsum, rows, hq, d);
+  } else if (!out_bf16 && in_bf16) {
+    hipLaunchKernelGGL((bwd_dsum_kernel<false, true>), grid, dim3(256), 0, st, out, dout, dsum, rows, hq, d);
+  } else if (!out_bf16 && !in_bf16) {
+    hipLaunchKernelGGL((bwd_dsum_kernel<false, false>), grid, dim3(256), 0, st, out, dout, dsum, rows, hq, d);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((ring_bwd_dq_bf16_kernel<D>), dim3((unsigned)a.nqt * (unsigned)a.hq), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((ring_bwd_dkv_bf16_kernel<D>), dim3((unsigned)(a.cp * a.nkt_kv) * (unsigned)a.hkv), dim3(256), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((ring_bwd_dq_f32_kernel<D>), dim3((unsigned)a.nqt * (unsigned)a.hq), dim3(64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((ring_bwd_dkv_f32_kernel<D>), dim3((unsigned)(a.cp * a.nkt_kv) * (unsigned)a.hkv), dim3(64), 0,
+                     st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_bwd(const BwdArgs& a, int d, int in_bf16, hipStream_t st) {
+  if (a.nqt == 0 || a.hq == 0) return hipSuccess;
+  if (in_bf16) {
+    if (d == 128) return launch_bwd_bf16<128>(a, st);
+    if (d == 64) return launch_bwd_bf16<64>(a, st);
+    return hipErrorInvalidValue;
+  }
+  if (d == 128) return launch_bwd_f32<128>(a, st);
+  if (d == 64) return launch_bwd_f32<64>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ra

@@ -97,6 +97,21 @@ __device__ __forceinline__ void row_interval(const int* cu, int n_docs, int s_to
   hi = causal ? pq : cu[d + 1] - 1;
 }
 
+// Visible query-position interval [lo, hi] of key position pk: the queries of
+// pk's document at or after pk (causal), or the whole document (non-causal).
+// The same relation as row_interval, solved for the query.
+__device__ __forceinline__ void key_interval(const int* cu, int n_docs, int s_total, int causal, int pk,
+                                             int& lo, int& hi) {
+  if (n_docs <= 1) {
+    lo = causal ? pk : 0;
+    hi = s_total - 1;
+    return;
+  }
+  const int d = doc_of(cu, n_docs, pk);
+  lo = causal ? pk : cu[d];
+  hi = cu[d + 1] - 1;
+}
+
 // Indices n in [0, cnt) with A <= start + stride*n <= B, as [n0, n1] (empty if n0 > n1).
 // Positions stay below 2^30, so 32-bit differences cannot overflow.
 __device__ __forceinline__ void run_range(const Run& r, int A, int B, int& n0, int& n1) {
@@ -192,6 +207,43 @@ struct AttnArgs {
   int nkt;
   int wl_stride;
   float scale_log2;   // softmax_scale * log2(e)
+};
+
+// Arguments of the backward kernels (one rank, all ring steps).
+struct BwdArgs {
+  const void* q;       // [S_l][hq][d]
+  const void* k;       // [cp][S_l][hkv][d]
+  const void* v;       // [cp][S_l][hkv][d]
+  const void* dout;    // [S_l][hq][d], same dtype as q
+  const float* lse;    // [hq][S_l] natural log, softmax over all ring steps
+  const float* dsum;   // [hq][S_l] sum_c dout * out per row
+  float* dq;           // [S_l][hq][d]
+  float* dk;           // [cp][S_l][hkv][d]
+  float* dv;           // [cp][S_l][hkv][d]
+  const int* cu;       // device cu_seqlens [n_docs+1] (unused when n_docs <= 1)
+  const int* wl;       // dQ kernel: the forward's work list [nqt][wl_stride]
+  const int* wl_count;
+  const int* order;
+  const int* kwl;      // dK/dV kernel: per key tile, the non-SKIP query tiles [cp*nkt_kv][kwl_stride]
+  const int* kwl_count;
+  const int* korder;   // key tiles, heaviest first
+  int n_docs;
+  int s_total;
+  int s_local;
+  int cp;
+  int rank;
+  int part;
+  int causal;
+  int hq;
+  int hkv;
+  int nqt;
+  int nkt;
+  int wl_stride;
+  int nkt_kv;          // key tiles per chunk (dK/dV kernel)
+  int nqt_kv;          // query tiles (dK/dV kernel)
+  int kwl_stride;
+  float scale;         // softmax_scale
+  float scale_log2;    // softmax_scale * log2(e)
 };
 
 }  // namespace ra

@@ -15,6 +15,8 @@ constexpr int32_t kMaxHeads = 4096;
 // Tile shapes of the attention kernels (must match the device code).
 constexpr int kBf16BM = 128, kBf16BN = 64;
 constexpr int kF32BM = 64, kF32BN = 32;
+constexpr int kBwdBf16BK = 128, kBwdBf16BQ = 64;
+constexpr int kBwdF32BK = 64, kBwdF32BQ = 32;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -83,6 +85,44 @@ Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev) {
   L.wl_off = align256(L.order_off + (size_t)L.nqt * 4);
   L.total = align256(L.wl_off + (size_t)L.nqt * L.wl_stride * 4);
   return L;
+}
+
+BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev) {
+  BwdLayout B{};
+  B.fwd = attn_layout(shape, cp_size, n_docs_dev);
+  const bool bf16 = shape->in_dtype == RA_BF16;
+  B.bk = bf16 ? kBwdBf16BK : kBwdF32BK;
+  B.bq = bf16 ? kBwdBf16BQ : kBwdF32BQ;
+  const int s_local = B.fwd.s_local;
+  B.nkt_kv = (s_local + B.bk - 1) / B.bk;
+  B.nqt_kv = (s_local + B.bq - 1) / B.bq;
+  B.kwl_stride = B.nqt_kv;
+  const size_t n_kt = (size_t)cp_size * B.nkt_kv;
+  B.kcount_off = B.fwd.total;
+  B.korder_off = align256(B.kcount_off + n_kt * 4);
+  B.kwl_off = align256(B.korder_off + n_kt * 4);
+  B.dsum_off = align256(B.kwl_off + n_kt * B.kwl_stride * 4);
+  B.total = align256(B.dsum_off + (size_t)shape->hq * s_local * 4);
+  return B;
+}
+
+ra_status check_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                         const void* dout, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
+                         int32_t partition, const ra_shape* shape, const float* dq, const float* dk, const float* dv,
+                         const void* workspace, size_t ws_bytes) {
+  if (!q || !k || !v || !out || !lse || !dout || !shape || !dq || !dk || !dv) return RA_ERR_NULL;
+  ra_status s = check_shape(shape, cp_size, rank, partition);
+  if (s != RA_OK) return s;
+  s = check_cu(cu, n_docs, shape->s_total);
+  if (s != RA_OK) return s;
+  // the fp32 gradients of one rank's rows and of one chunk stay within 2^31 bytes
+  const int64_t heads = shape->hq > shape->hkv ? shape->hq : shape->hkv;
+  if ((shape->s_total / cp_size) * heads * shape->d * 4 > 0x7fffffffLL) return RA_ERR_SHAPE;
+  const BwdLayout B = bwd_layout(shape, cp_size, effective_docs(cu, n_docs));
+  if ((int64_t)B.fwd.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
+  if ((int64_t)cp_size * B.nkt_kv * shape->hkv > 0x7fffffffLL) return RA_ERR_SHAPE;
+  if (!workspace || ws_bytes < B.total) return RA_ERR_WORKSPACE;
+  return RA_OK;
 }
 
 ra_status check_forward(const void* q, const void* k, const void* v, const int32_t* cu, int32_t n_docs,

@@ -17,6 +17,16 @@ struct Layout {
   size_t cu_off, count_off, order_off, wl_off, total;
 };
 
+// Workspace of ra_backward: the forward's plan (dQ kernel), the key-side plan
+// of the dK/dV kernel, and the per-row sums D = dO . O.
+struct BwdLayout {
+  Layout fwd;
+  int bk, bq;          // dK/dV kernel tile: keys per workgroup x query rows per tile
+  int nkt_kv, nqt_kv;  // key tiles per chunk, query tiles
+  int kwl_stride;      // entries reserved per key tile (nqt_kv)
+  size_t kcount_off, korder_off, kwl_off, dsum_off, total;
+};
+
 // Shape checks shared by the attention entry points (no pointer checks).
 ra_status check_shape(const ra_shape* shape, int32_t cp_size, int32_t rank, int32_t partition);
 
@@ -25,6 +35,15 @@ ra_status check_cu(const int32_t* cu, int32_t n_docs, int64_t s_total);
 
 // Workspace layout of ra_forward / ra_forward_steps for a validated shape.
 Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev);
+
+// Workspace layout of ra_backward for a validated shape.
+BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev);
+
+// Full validation of ra_backward arguments.
+ra_status check_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                         const void* dout, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
+                         int32_t partition, const ra_shape* shape, const float* dq, const float* dk, const float* dv,
+                         const void* workspace, size_t ws_bytes);
 
 // Number of documents the kernels see for a validated cu_seqlens argument.
 int32_t effective_docs(const int32_t* cu, int32_t n_docs);

@@ -12,10 +12,17 @@ constexpr int kAttnBf16BN = 64;
 constexpr int kAttnF32BM = 64;
 constexpr int kAttnF32BN = 32;
 
+// Tile shapes of the dK/dV kernels (keys per workgroup x query rows per tile).
+constexpr int kBwdBf16BK = 128;
+constexpr int kBwdBf16BQ = 64;
+constexpr int kBwdF32BK = 64;
+constexpr int kBwdF32BQ = 32;
+
 // Largest batch of cu_seqlens entries passed by value to the upload kernel.
 constexpr int kCuChunk = 960;
 
 struct AttnArgs;
+struct BwdArgs;
 
 hipError_t launch_ring_attn(const AttnArgs& a, int d, int in_bf16, int out_bf16, int steps, hipStream_t st);
 
@@ -26,6 +33,23 @@ hipError_t launch_upload_i32(const int32_t* host, int n, int32_t* dst, hipStream
 hipError_t launch_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
                            int causal, int bm, int bn, int nqt, int nkt, int wl_stride, int* wl, int* wl_count,
                            int* order, hipStream_t st);
+
+// Orders n tiles by descending count (ties by index) into order[0..n).
+hipError_t launch_order(const int* count, int n, int* order, hipStream_t st);
+
+// Key-side work list of the dK/dV kernels: for key tile kt = s * nkt + J (keys
+// [J bk, (J+1) bk) of chunk s), the non-SKIP query tiles of `rank`; then the
+// heaviest-first key-tile order.
+hipError_t launch_kv_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
+                              int causal, int bq, int bk, int nqt, int nkt, int stride, int* wl, int* count,
+                              int* order, hipStream_t st);
+
+// dsum[h][i] = sum_c dout[i][h][c] * out[i][h][c] (fp32).
+hipError_t launch_bwd_dsum(const void* out, const void* dout, float* dsum, int rows, int hq, int d, int out_bf16,
+                           int in_bf16, hipStream_t st);
+
+// dQ kernel then dK/dV kernel.
+hipError_t launch_ring_bwd(const BwdArgs& a, int d, int in_bf16, hipStream_t st);
 
 hipError_t launch_classify(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
                            int causal, int bm, int bn, int nqt, int nkt, int8_t* cls, hipStream_t st);

@@ -23,7 +23,7 @@ from typing import Optional
 import numpy as np
 
 # Tensor identifiers used to derive independent random streams.
-TID_Q, TID_K, TID_V, TID_DOCS = 1, 2, 3, 4
+TID_Q, TID_K, TID_V, TID_DOCS, TID_DOUT = 1, 2, 3, 4, 5
 
 PARTITIONS = ("contiguous", "zigzag", "striped")
 
@@ -178,6 +178,15 @@ def make_global_inputs(w: Workload, seed: int = 0, s_total: Optional[int] = None
         v = normal_f32(seed, TID_V, (S, w.hkv, w.d), ps)
     cu = loguniform_cu_seqlens(seed, S, w.doc_lo, w.doc_hi) if w.docs == "loguniform" else None
     return GlobalInputs(q, k, v, cu, w.dtype)
+
+
+def make_global_dout(w: Workload, seed: int = 0, s_total: Optional[int] = None) -> np.ndarray:
+    """Seeded upstream gradient dO [S, hq, d] in global order, N(0,1) (bf16 bits
+    for bf16 workloads, fp32 values otherwise)."""
+    S = int(s_total or w.s_total)
+    if w.dtype == "bf16":
+        return normal_bf16_bits(seed, TID_DOUT, (S, w.hq, w.d))
+    return normal_f32(seed, TID_DOUT, (S, w.hq, w.d))
 
 
 def make_ulysses_inputs(n: int, s_local: int, h: int, d: int, seed: int = 0, tid: int = TID_Q) -> np.ndarray:

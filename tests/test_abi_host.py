@@ -150,3 +150,36 @@ def test_permute_validation():
     assert lib.cp_reorder(P, P2, 1024, 32, 128, 2, 4, 5, 0, None) == ra.RA_ERR_UNSUPPORTED
     assert lib.cp_reorder(P, P2, 1024, 32, 128, 2, 4, 1, 2, None) == ra.RA_ERR_SHAPE
     assert lib.cp_reorder(None, P2, 1024, 32, 128, 2, 4, 1, 0, None) == ra.RA_ERR_NULL
+
+
+def bwd(sh, cu=None, n_docs=0, cp=4, rank=0, part=1, ws=P, ws_bytes=1 << 40, q=P, out=P, lse=P, dout=P, dq=P,
+        dk=P, dv=P):
+    arr = None
+    if cu is not None:
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+    return _lib().ra_backward(q, P, P, out, lse, dout, arr, n_docs, cp, rank, part, ctypes.byref(sh), dq, dk, dv,
+                              ws, ws_bytes, None)
+
+
+def test_backward_validation_codes():
+    for kw in ("q", "out", "lse", "dout", "dq", "dk", "dv"):
+        assert bwd(shape(), **{kw: None}) == ra.RA_ERR_NULL, kw
+    assert _lib().ra_backward(P, P, P, P, P, P, None, 0, 4, 0, 1, None, P, P, P, P, 1 << 40, None) == ra.RA_ERR_NULL
+    assert bwd(shape(s_total=0)) == ra.RA_ERR_SHAPE
+    assert bwd(shape(), rank=4) == ra.RA_ERR_RANK
+    assert bwd(shape(hq=32, hkv=5)) == ra.RA_ERR_HEADS
+    assert bwd(shape(d=80)) == ra.RA_ERR_UNSUPPORTED
+    assert bwd(shape(), part=7) == ra.RA_ERR_UNSUPPORTED
+    assert bwd(shape(s_total=4 * 1001), part=1) == ra.RA_ERR_DIVISIBILITY
+    assert bwd(shape(s_total=64, hq=2, hkv=2), cu=[0, 70, 64], n_docs=2) == ra.RA_ERR_CU_SEQLENS
+    # fp32 gradients of one rank's rows must stay below 2^31 bytes (bf16 inputs pass the forward's bound)
+    big = shape(s_total=4 * 65536, hq=64, hkv=64, d=128)
+    assert bwd(big) == ra.RA_ERR_SHAPE
+    sh = shape()
+    need = ra.ra_backward_workspace_size(sh, 4, 0)
+    assert need > ra.ra_workspace_size(sh, 4, 0)
+    assert bwd(sh, ws=None) == ra.RA_ERR_WORKSPACE
+    assert bwd(sh, ws_bytes=need - 1) == ra.RA_ERR_WORKSPACE
+    assert ra.ra_backward_workspace_size(shape(s_total=0), 4, 0) == 0
+    assert _lib().ra_backward_workspace_size(None, 4, 0) == 0
+    assert ra.ra_backward_workspace_size(sh, 4, 50) > need
