@@ -147,7 +147,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-every", type=int, default=16)
-    ap.add_argument("--mode", default="full", choices=["full", "attn-only", "copy-only"],
+    ap.add_argument("--mode", default="full", choices=["full", "attn-only", "bwd-only", "copy-only"],
                     help="attn-only / copy-only: a few launches of one kernel, for counter runs")
     args = ap.parse_args()
 
@@ -211,6 +211,18 @@ def main():
         print(json.dumps({"mode": "attn-only", "launches": 24, "flops_per_launch": flops}))
         return
 
+    if args.mode == "bwd-only":
+        ra.cp_reorder(q_g, cp, w.partition, out=q_p)
+        ra.cp_reorder(k_g, cp, w.partition, out=k_p)
+        ra.cp_reorder(v_g, cp, w.partition, out=v_p)
+        ra.ra_forward(q_p[rank], k_p, v_p, None, cp, rank, w.partition, out=out, lse=lse, workspace=ws)
+        bw = backward_buffers(torch, ra, w, dev)
+        for _ in range(12):
+            run_backward(ra, w, q_p[rank], k_p, v_p, out, lse, bw)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "bwd-only", "launches": 12, "flops_per_launch": 2.5 * flops}))
+        return
+
     def step():
         ra.cp_reorder(q_g, cp, w.partition, out=q_p)
         ra.cp_reorder(k_g, cp, w.partition, out=k_p)
@@ -250,6 +262,20 @@ def main():
     log(f"attention kernel {attn['avg_ms']:.3f} ms = {attn_tflops:.1f} TFLOP/s; "
         f"cp_reorder {kernels['cp_reorder_k_s32k_h32_zigzag']['gbs']:.0f} GB/s")
 
+    # backward of the same share: dQ, and this rank's dK / dV partials of every chunk
+    bw = backward_buffers(torch, ra, w, dev)
+    tb = time_events(torch, lambda: run_backward(ra, w, q_p[rank], k_p, v_p, out, lse, bw), max(5, args.steps // 2))
+    bflops = 2.5 * flops
+    kernels["ring_attn_backward_llama7b_zigzag_rank0"] = {
+        "avg_ms": tb["avg_ms"], "min_ms": tb["min_ms"], "flops": bflops,
+        "tflops": bflops / (tb["avg_ms"] * 1e-3) / 1e12,
+        "frac_bf16_peak": bflops / (tb["avg_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "mfma_tflops_executed": 3.5 * flops / (tb["avg_ms"] * 1e-3) / 1e12,
+        "note": "whole ra_backward call (plans, D = dO.O, dQ kernel, dK/dV kernel); FLOPs = 2.5 x forward"}
+    log(f"backward {tb['avg_ms']:.3f} ms = {kernels['ring_attn_backward_llama7b_zigzag_rank0']['tflops']:.1f} "
+        f"TFLOP/s (2.5 x forward FLOPs)")
+    del bw
+
     if not args.no_extras:
         kernels.update(extras(np, torch, ra, synth, dev, max(5, args.steps // 2)))
 
@@ -277,6 +303,24 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
+
+
+def backward_buffers(torch, ra, w, dev):
+    """dO (seeded on the GPU), gradient outputs and workspace of one rank's backward."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    sl = w.s_total // w.cp
+    shape = ra.make_shape(w.s_total, w.hq, w.hkv, w.d, True, 0.0, ra.RA_BF16, ra.RA_BF16)
+    return {"dout": torch.randn((sl, w.hq, w.d), device=dev, dtype=torch.bfloat16, generator=gen),
+            "dq": torch.empty((sl, w.hq, w.d), device=dev, dtype=torch.float32),
+            "dk": torch.empty((w.cp, sl, w.hkv, w.d), device=dev, dtype=torch.float32),
+            "dv": torch.empty((w.cp, sl, w.hkv, w.d), device=dev, dtype=torch.float32),
+            "ws": torch.empty(ra.ra_backward_workspace_size(shape, w.cp, 0), device=dev, dtype=torch.uint8)}
+
+
+def run_backward(ra, w, q, k, v, out, lse, bw, cu=None, rank=None):
+    return ra.ra_backward(q, k, v, out, lse, bw["dout"], cu, w.cp, w.rank if rank is None else rank, w.partition,
+                          dq=bw["dq"], dk=bw["dk"], dv=bw["dv"], workspace=bw["ws"])
 
 
 def extras(np, torch, ra, synth, dev, reps):

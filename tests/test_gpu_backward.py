@@ -19,7 +19,6 @@ up to ~1000 terms (n * 2^-24 relative) and fp32 dP - D cancellation are the
 only error sources there.
 """
 import itertools
-import math
 
 import numpy as np
 import pytest
@@ -28,119 +27,10 @@ import torch
 import oracle
 import sequence_parallelism_amd as ra
 import synth
-from oracle import backward as obwd
-from tests.gpu_common import oracle_inputs, rank_inputs, to_device
+from tests.bwd_common import SLACK, Ref, bwd_case, check_bound, check_rank, run_backward
+from tests.gpu_common import rank_inputs, to_device
 
 pytestmark = pytest.mark.gpu
-
-SLACK = 1e-5
-
-
-def _case(S, hq, hkv, d, dtype, seed, docs=None):
-    w = synth.Workload("bwd_case", S, hq, hkv, d, 1, "contiguous", 0, dtype, docs=docs, doc_lo=16,
-                       doc_hi=max(17, S // 3))
-    return synth.make_global_inputs(w, seed), synth.make_global_dout(w, seed)
-
-
-def _bf16_round(x):
-    return synth.bf16_bits_to_f64(synth.f32_to_bf16_bits(np.asarray(x, dtype=np.float32)))
-
-
-class Ref:
-    """Oracle forward + gradients of one rank, and per-element rounding bounds."""
-
-    def __init__(self, g, gdo, cp, rank, part, causal=True, scale=None, rows=None):
-        S = g.q.shape[0]
-        self.gq, self.gk, self.gv = oracle_inputs(g)
-        pos = oracle.positions(part, S, cp, rank)
-        self.rows = np.arange(len(pos)) if rows is None else np.asarray(rows)
-        self.pos = pos[self.rows]
-        self.dout = synth.to_f64(gdo, g.dtype)[self.pos]
-        self.cu, self.S, self.causal = g.cu_seqlens, S, causal
-        d = self.gq.shape[2]
-        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
-        qr = self.gq[self.pos]
-        keys = np.arange(S)
-        self.O, self.L = oracle.attention_rows(qr, self.pos, self.gk, self.gv, keys, self.cu, S, causal, self.scale)
-        self.dq, self.dk, self.dv = oracle.attention_rows_backward(qr, self.pos, self.gk, self.gv, keys, self.dout,
-                                                                   self.cu, S, causal, self.scale)
-        hq, hkv = qr.shape[1], self.gk.shape[1]
-        G = hq // hkv
-        R = len(self.pos)
-        self.A_dq = np.zeros((R, hq, d))
-        self.A_dk = np.zeros((S, hkv, d))
-        self.A_dv = np.zeros((S, hkv, d))
-        self.PK = np.zeros((R, hq, d))   # sum_k P_ik |k_k|
-        self.PV = np.zeros((R, hq, d))   # sum_k P_ik |v_k|
-        self._P = []
-        for h in range(hq):
-            gh = h // G
-            P, _, dS = obwd.softmax_grad_terms(qr, self.pos, self.gk, self.gv, keys, self.dout, self.cu, S, h,
-                                               causal, self.scale)
-            self.A_dq[:, h] = self.scale * (np.abs(dS) @ np.abs(self.gk[:, gh]))
-            self.A_dk[:, gh] += self.scale * (np.abs(dS).T @ np.abs(qr[:, h]))
-            self.A_dv[:, gh] += P.T @ np.abs(self.dout[:, h])
-            self.PK[:, h] = P @ np.abs(self.gk[:, gh])
-            self.PV[:, h] = P @ np.abs(self.gv[:, gh])
-            self._P.append(P)
-
-    def d_error_bounds(self, eD):
-        """Extra bounds on dQ [R,hq,d] and dK [S,hkv,d] from an error |dD_i| <= eD [R,hq]."""
-        hq, hkv = self.dq.shape[1], self.dk.shape[1]
-        G = hq // hkv
-        xq = self.scale * eD[:, :, None] * self.PK
-        xk = np.zeros_like(self.dk)
-        qr = self.gq[self.pos]
-        for h in range(hq):
-            xk[:, h // G] += self.scale * (self._P[h].T @ (eD[:, h, None] * np.abs(qr[:, h])))
-        return xq, xk
-
-    def chunked(self, x, part, cp):
-        """Global-order [S,hkv,d] -> rank-major chunks [cp,S_l,hkv,d]."""
-        return np.stack([x[oracle.positions(part, self.S, cp, s)] for s in range(cp)])
-
-
-def _check(name, got, ref, bound):
-    got = np.asarray(got, dtype=np.float64)
-    assert np.all(np.isfinite(got)), f"{name}: non-finite"
-    err = np.abs(got - ref)
-    ratio = err / bound
-    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
-    assert ratio.max() <= 1.0, (f"{name}: error {err[worst]:.3e} > bound {bound[worst]:.3e} at {worst} "
-                                f"(ref {ref[worst]:.4e}); max-abs err {err.max():.3e}")
-    return float(err.max())
-
-
-def _run_gpu(g, gdo, cp, rank, part, O, L, causal=True, out_dtype=torch.float32, scale=0.0):
-    qr, kr, vr = rank_inputs(g, cp, rank, part)
-    do = ra.cp_reorder(to_device(gdo, g.dtype), cp, part)[rank].contiguous()
-    if out_dtype == torch.bfloat16:
-        out = to_device(synth.f32_to_bf16_bits(np.asarray(O, dtype=np.float32)), "bf16")
-    else:
-        out = torch.from_numpy(np.asarray(O, dtype=np.float32)).cuda()
-    lse = torch.from_numpy(np.asarray(L, dtype=np.float32)).cuda()
-    dq, dk, dv = ra.ra_backward(qr, kr, vr, out, lse, do, g.cu_seqlens, cp, rank, part, causal=causal,
-                                softmax_scale=scale)
-    torch.cuda.synchronize()
-    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
-
-
-def _check_rank(g, gdo, cp, rank, part, causal=True, out_dtype=torch.float32, rel=2.0 ** -8, slack=SLACK):
-    ref = Ref(g, gdo, cp, rank, part, causal)
-    dq, dk, dv = _run_gpu(g, gdo, cp, rank, part, ref.O, ref.L, causal, out_dtype)
-    bq = rel * ref.A_dq + slack
-    bk = rel * ref.A_dk + slack
-    bv = rel * ref.A_dv + slack
-    if out_dtype == torch.bfloat16:
-        # D is computed from O rounded to bf16: |dD_i| <= sum_c |dO_ic| |O_ic - bf16(O_ic)|
-        eD = np.abs(ref.dout * (ref.O - _bf16_round(ref.O))).sum(axis=2)
-        xq, xk = ref.d_error_bounds(eD)
-        bq, bk = bq + 2 * xq, bk + 2 * xk
-    e = (_check("dq", dq, ref.dq, bq),
-         _check("dk", dk, ref.chunked(ref.dk, part, cp), ref.chunked(bk, part, cp)),
-         _check("dv", dv, ref.chunked(ref.dv, part, cp), ref.chunked(bv, part, cp)))
-    return ref, e
-
 
 SMALL = list(itertools.product(["contiguous", "zigzag", "striped"], [1, 2, 4, 8], [False, True]))
 
@@ -148,9 +38,9 @@ SMALL = list(itertools.product(["contiguous", "zigzag", "striped"], [1, 2, 4, 8]
 @pytest.mark.parametrize("part,cp,docs", SMALL)
 def test_backward_small_bf16_partitions(part, cp, docs):
     """bf16, d=128, GQA 4:2, S=2048: ranks 0, CP/2 and CP-1, every row and key."""
-    g, gdo = _case(2048, 4, 2, 128, "bf16", seed=100 + cp * 10 + docs, docs="loguniform" if docs else None)
+    g, gdo = bwd_case(2048, 4, 2, 128, "bf16", seed=100 + cp * 10 + docs, docs="loguniform" if docs else None)
     for rank in sorted({0, cp // 2, cp - 1}):
-        _check_rank(g, gdo, cp, rank, part)
+        check_rank(g, gdo, cp, rank, part)
 
 
 @pytest.mark.parametrize("part", ["contiguous", "zigzag", "striped"])
@@ -158,31 +48,31 @@ def test_backward_ragged_and_noncausal(part):
     """S_l = 346 (not a multiple of the 64-row, 128-key or 64-key tiles), zigzag
     halves straddling tiles, documents, causal and document-only masks."""
     cp = 4
-    g, gdo = _case(2 * cp * 173, 2, 1, 128, "bf16", seed=107, docs="loguniform")
+    g, gdo = bwd_case(2 * cp * 173, 2, 1, 128, "bf16", seed=107, docs="loguniform")
     for rank in range(cp):
-        _check_rank(g, gdo, cp, rank, part, causal=True)
-        _check_rank(g, gdo, cp, rank, part, causal=False)
+        check_rank(g, gdo, cp, rank, part, causal=True)
+        check_rank(g, gdo, cp, rank, part, causal=False)
 
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("out_bf16", [False, True])
 def test_backward_head_dims_and_output_dtypes(d, out_bf16):
-    g, gdo = _case(1024, 2, 2, d, "bf16", seed=111)
-    _check_rank(g, gdo, 2, 1, "zigzag", out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    g, gdo = bwd_case(1024, 2, 2, d, "bf16", seed=111)
+    check_rank(g, gdo, 2, 1, "zigzag", out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
 
 
 def test_backward_gqa_striped_cp8():
-    g, gdo = _case(4096, 8, 2, 128, "bf16", seed=113, docs="loguniform")
+    g, gdo = bwd_case(4096, 8, 2, 128, "bf16", seed=113, docs="loguniform")
     for rank in (0, 5, 7):
-        _check_rank(g, gdo, 8, rank, "striped")
+        check_rank(g, gdo, 8, rank, "striped")
 
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_fp32_inputs(d):
     """fp32 inputs take the VALU kernels: no bf16 rounding anywhere."""
-    g, gdo = _case(768, 2, 1, d, "f32", seed=115, docs="loguniform")
+    g, gdo = bwd_case(768, 2, 1, d, "f32", seed=115, docs="loguniform")
     for rank in range(3):
-        _check_rank(g, gdo, 3, rank, "striped", rel=2.0 ** -12, slack=1e-4)
+        check_rank(g, gdo, 3, rank, "striped", rel=2.0 ** -12, slack=1e-4)
 
 
 def test_backward_tiny_ring_fp32():
@@ -191,26 +81,26 @@ def test_backward_tiny_ring_fp32():
     g = synth.make_global_inputs(w, 0)
     gdo = synth.make_global_dout(w, 0)
     for rank in (2, 0, 1, 3):
-        _check_rank(g, gdo, 4, rank, "contiguous", rel=2.0 ** -12, slack=1e-4)
+        check_rank(g, gdo, 4, rank, "contiguous", rel=2.0 ** -12, slack=1e-4)
 
 
 def test_backward_ranks_sum_to_whole_sequence_gradient():
     """A real ring adds every rank's dK / dV partial as the chunk travels: the sum
     over ranks equals the gradient of attention over the whole sequence (CP = 1)."""
     cp, part = 4, "zigzag"
-    g, gdo = _case(2048, 4, 2, 128, "bf16", seed=117, docs="loguniform")
+    g, gdo = bwd_case(2048, 4, 2, 128, "bf16", seed=117, docs="loguniform")
     dk_sum = dv_sum = 0
     bk_sum = bv_sum = 0
     for rank in range(cp):
         ref = Ref(g, gdo, cp, rank, part)
-        _, dk, dv = _run_gpu(g, gdo, cp, rank, part, ref.O, ref.L)
+        _, dk, dv = run_backward(g, gdo, cp, rank, part, ref.O, ref.L)
         dk_sum = dk_sum + dk
         dv_sum = dv_sum + dv
         bk_sum = bk_sum + ref.chunked(2.0 ** -8 * ref.A_dk + SLACK, part, cp)
         bv_sum = bv_sum + ref.chunked(2.0 ** -8 * ref.A_dv + SLACK, part, cp)
     full = Ref(g, gdo, 1, 0, "contiguous")
-    _check("sum dk", dk_sum, full.chunked(full.dk, part, cp), bk_sum)
-    _check("sum dv", dv_sum, full.chunked(full.dv, part, cp), bv_sum)
+    check_bound("sum dk", dk_sum, full.chunked(full.dk, part, cp), bk_sum)
+    check_bound("sum dv", dv_sum, full.chunked(full.dv, part, cp), bv_sum)
 
 
 def test_backward_after_gpu_forward():
@@ -218,7 +108,7 @@ def test_backward_after_gpu_forward():
     its O and LSE. The forward rounds P to bf16, so |O - O_exact| <= 2^-8 sum_k P|v|
     per element, which bounds the error of D = dO . O."""
     cp, rank, part = 4, 1, "zigzag"
-    g, gdo = _case(2048, 4, 4, 128, "bf16", seed=119, docs="loguniform")
+    g, gdo = bwd_case(2048, 4, 4, 128, "bf16", seed=119, docs="loguniform")
     ref = Ref(g, gdo, cp, rank, part)
     qr, kr, vr = rank_inputs(g, cp, rank, part)
     out, lse = ra.ra_forward(qr, kr, vr, g.cu_seqlens, cp, rank, part, out_dtype=torch.float32)
@@ -230,19 +120,19 @@ def test_backward_after_gpu_forward():
     # The forward's LSE is within its own parity bar (1e-3), which scales a row's P
     # by at most e^(1e-3): a relative 1e-3 of every term of dS and P.
     r = 2.0 ** -8 + 1e-3
-    _check("dq", dq.cpu().numpy(), ref.dq, r * ref.A_dq + xq + SLACK)
-    _check("dk", dk.cpu().numpy(), ref.chunked(ref.dk, part, cp), ref.chunked(r * ref.A_dk + xk + SLACK, part, cp))
-    _check("dv", dv.cpu().numpy(), ref.chunked(ref.dv, part, cp), ref.chunked(r * ref.A_dv + SLACK, part, cp))
+    check_bound("dq", dq.cpu().numpy(), ref.dq, r * ref.A_dq + xq + SLACK)
+    check_bound("dk", dk.cpu().numpy(), ref.chunked(ref.dk, part, cp), ref.chunked(r * ref.A_dk + xk + SLACK, part, cp))
+    check_bound("dv", dv.cpu().numpy(), ref.chunked(ref.dv, part, cp), ref.chunked(r * ref.A_dv + SLACK, part, cp))
 
 
 def test_backward_invisible_keys_and_determinism():
     """Keys that no row of the rank sees get exactly zero dK / dV; changing K / V
     at those positions leaves dQ bit-identical; repeated calls are bit-identical."""
     cp, rank, part = 4, 1, "zigzag"
-    g, gdo = _case(2048, 2, 2, 128, "bf16", seed=121, docs="loguniform")
+    g, gdo = bwd_case(2048, 2, 2, 128, "bf16", seed=121, docs="loguniform")
     ref = Ref(g, gdo, cp, rank, part)
-    dq1, dk1, dv1 = _run_gpu(g, gdo, cp, rank, part, ref.O, ref.L)
-    dq1b, dk1b, dv1b = _run_gpu(g, gdo, cp, rank, part, ref.O, ref.L)
+    dq1, dk1, dv1 = run_backward(g, gdo, cp, rank, part, ref.O, ref.L)
+    dq1b, dk1b, dv1b = run_backward(g, gdo, cp, rank, part, ref.O, ref.L)
     assert np.array_equal(dq1, dq1b) and np.array_equal(dk1, dk1b) and np.array_equal(dv1, dv1b)
     vis = oracle.visible_matrix(ref.pos, np.arange(2048), g.cu_seqlens, 2048, True).any(axis=0)
     inv_chunks = ref.chunked(~vis[:, None, None] & np.ones((2048, 2, 128), bool), part, cp)
@@ -252,7 +142,7 @@ def test_backward_invisible_keys_and_determinism():
     noise = synth.normal_bf16_bits(99, 9, g.k.shape, 30.0)
     g2.k[~vis] = noise[~vis]
     g2.v[~vis] = noise[~vis][:, :, ::-1]
-    dq2, dk2, dv2 = _run_gpu(g2, gdo, cp, rank, part, ref.O, ref.L)
+    dq2, dk2, dv2 = run_backward(g2, gdo, cp, rank, part, ref.O, ref.L)
     assert np.array_equal(dq1, dq2)
     vis_chunks = ~inv_chunks
     assert np.array_equal(dk1[vis_chunks], dk2[vis_chunks]) and np.array_equal(dv1[vis_chunks], dv2[vis_chunks])
