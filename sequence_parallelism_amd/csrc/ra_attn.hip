@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
     if (do_tile && need_mask) {
       tm = tile_mask(pinfo, ring_owner(a.rank, t, a.cp), ka, kb, cls, row_ok, lo, hi);
       do_tile = __any(tm.la > 0 || tm.lb > 0);
-      need_mask = !__all((tm.i0a == 0 && tm.la == BN) || !row_ok);
+      need_mask = !__all(tile_all_visible(tm, BN) || !row_ok);
     }
 
     if (do_tile) {

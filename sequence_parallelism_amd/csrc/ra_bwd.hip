@@ -199,6 +199,25 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
     }
   };
 
+  // Per-lane LDS element offsets at key rows 0..31 (swz_rt is unchanged by a shift of 16
+  // rows, so the second 32-key half and the 16-row steps only add constants):
+  //   rd_off[j]      row-wise read of row l32, logical chunk 2 j + hi32 (A operand of S^T, dP^T)
+  //   tr0/1_off[c]   transposing reads of rows 4 hi32 + (lane % 16) / 4 and 8 more, columns
+  //                  32 c + 16 ((lane / 16) % 2) + 4 (lane % 4) (A operand of dQ^T)
+  int rd_off[NKD], tr0_off[NCT], tr1_off[NCT];
+#pragma unroll
+  for (int j = 0; j < NKD; ++j) {
+    const int kc = 2 * j + hi32;
+    rd_off[j] = l32 * ROW + 8 * (DMA ? (kc ^ swz_rt(l32)) : kc);
+  }
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int r0 = 4 * hi32 + ((lane & 15) >> 2);
+    const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    tr0_off[c] = r0 * ROW + (DMA ? ((((c0 >> 3) ^ swz_rt(r0)) << 3) | (c0 & 7)) : c0);
+    tr1_off[c] = (r0 + 8) * ROW + (DMA ? ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7)) : c0);
+  }
+
   if (n_ent > 0) {
     load_tile(list[0], 0);
     store_tile(0);
@@ -219,7 +238,7 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
     if (do_tile && need_mask) {
       tm = tile_mask(pinfo, ring_owner(a.rank, t, a.cp), ka, kb, cls, row_ok, lo, hi);
       do_tile = __any(tm.la > 0 || tm.lb > 0);
-      need_mask = !__all((tm.i0a == 0 && tm.la == BN) || !row_ok);
+      need_mask = !__all(tile_all_visible(tm, BN) || !row_ok);
     }
 
     if (do_tile) {
@@ -231,24 +250,32 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
       for (int j = 0; j < NKD; ++j)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const int kr = kt * 32 + l32, kc = 2 * j + hi32;
-          const int o = kr * ROW + 8 * (DMA ? (kc ^ swz_rt(kr)) : kc);
+          const int o = kt * 32 * ROW + rd_off[j];
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ks + o), qreg[j], s[kt], 0, 0, 0);
           dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vs + o), oreg[j], dp[kt], 0, 0, 0);
         }
       __builtin_amdgcn_s_setprio(0);
       // lane holds keys n = 32 kt + 8 (i/4) + 4 hi32 + (i%4) of its row; dS^T in place of S^T
-      const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+      if (!need_mask) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int n = kt * 32 + 8 * (i >> 2) + (i & 3);
-          const bool vis =
-              !need_mask || ((unsigned)(n + ba) < (unsigned)tm.la) | ((unsigned)(n + bb) < (unsigned)tm.lb);
-          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], C, -lse2)) : 0.f;
-          s[kt][i] = vis ? p * (dp[kt][i] - dsum) : 0.f;
-        }
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], C, -lse2));
+            s[kt][i] = p * (dp[kt][i] - dsum);
+          }
+      } else {
+        const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int n = kt * 32 + 8 * (i >> 2) + (i & 3);
+            const bool vis = ((unsigned)(n + ba) < (unsigned)tm.la) | ((unsigned)(n + bb) < (unsigned)tm.lb);
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], C, -lse2)) : 0.f;
+            s[kt][i] = vis ? p * (dp[kt][i] - dsum) : 0.f;
+          }
+      }
       // dQ^T += K^T dS^T
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -259,16 +286,9 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
         for (int c = 0; c < NCT; ++c)
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
-            const int r0 = kt * 32 + jj * 16 + 4 * hi32 + ((lane & 15) >> 2);
-            const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            int o0 = r0 * ROW + c0, o1 = (r0 + 8) * ROW + c0;
-            if constexpr (DMA) {
-              o0 = r0 * ROW + ((((c0 >> 3) ^ swz_rt(r0)) << 3) | (c0 & 7));
-              o1 = (r0 + 8) * ROW + ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7));
-            }
-            const bf16x4 k0 = lds_read_tr(ks + o0);
-            const bf16x4 k1 = lds_read_tr(ks + o1);
-            const bf16x8 kk = __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const int ro = (kt * 32 + jj * 16) * ROW;
+            const bf16x8 kk = __builtin_shufflevector(lds_read_tr(ks + ro + tr0_off[c]),
+                                                      lds_read_tr(ks + ro + tr1_off[c]), 0, 1, 2, 3, 4, 5, 6, 7);
             acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, jj ? sb1 : sb0, acc[c], 0, 0, 0);
           }
       }
@@ -423,6 +443,25 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
     }
   };
 
+  // Per-lane LDS element offsets at qh = 0, jj = 0. swz_rt is unchanged by a shift of
+  // 16 rows, so the 32-row halves and 16-row steps only add constants:
+  //   rd_off[j]      row-wise read of row l32, logical chunk 2 j + hi32 (A operand of X, dP)
+  //   tr0/1_off[c]   transposing reads of rows 4 hi32 + (lane % 16) / 4 and 8 more, columns
+  //                  32 c + 16 ((lane / 16) % 2) + 4 (lane % 4) (A operand of dV^T, dK^T)
+  int rd_off[NKD], tr0_off[NCT], tr1_off[NCT];
+#pragma unroll
+  for (int j = 0; j < NKD; ++j) {
+    const int kc = 2 * j + hi32;
+    rd_off[j] = l32 * ROW + 8 * (DMA ? (kc ^ swz_rt(l32)) : kc);
+  }
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int r0 = 4 * hi32 + ((lane & 15) >> 2);
+    const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    tr0_off[c] = r0 * ROW + (DMA ? ((((c0 >> 3) ^ swz_rt(r0)) << 3) | (c0 & 7)) : c0);
+    tr1_off[c] = (r0 + 8) * ROW + (DMA ? ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7)) : c0);
+  }
+
   if (total > 0) {
     load_tile(0, 0);
     store_tile(0);
@@ -443,7 +482,7 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
     if (do_tile && need_mask) {
       tm = tile_mask(pinfo, a.rank, qa, qb, cls, key_ok, plo, phi);
       do_tile = __any(tm.la > 0 || tm.lb > 0);
-      need_mask = !__all((tm.i0a == 0 && tm.la == BQ) || !key_ok);
+      need_mask = !__all(tile_all_visible(tm, BQ) || !key_ok);
     }
 
     if (do_tile) {
@@ -452,33 +491,48 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
       const __bf16* os = qs + TILE;
       const float* l2s = rowv[buf][0];
       const float* dss = rowv[buf][1];
-#pragma unroll
+#pragma unroll 1
       for (int qh = 0; qh < 2; ++qh) {
+        const __bf16* qh_q = qs + qh * 32 * ROW;
+        const __bf16* qh_o = os + qh * 32 * ROW;
         f32x16 x = f32x16{}, dp = f32x16{};
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < NKD; ++j) {
-          const int qr = qh * 32 + l32, kc = 2 * j + hi32;
-          const int o = qr * ROW + 8 * (DMA ? (kc ^ swz_rt(qr)) : kc);
-          x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qs + o), kreg[j], x, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(os + o), vreg[j], dp, 0, 0, 0);
+          x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qh_q + rd_off[j]), kreg[j], x, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qh_o + rd_off[j]), vreg[j], dp, 0, 0, 0);
         }
         __builtin_amdgcn_s_setprio(0);
-        // lane holds query rows n = 32 qh + 8 (i/4) + 4 hi32 + (i%4) of its key: P in x, dS in dp
-        const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+        // lane holds query rows n = 32 qh + 8 (i/4) + 4 hi32 + (i%4) of its key: P into x, dS into dp
+        if (!need_mask) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int n0 = qh * 32 + 8 * i4 + 4 * hi32;
-          const f32x4 L = *(const f32x4*)(l2s + n0);
-          const f32x4 Dd = *(const f32x4*)(dss + n0);
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int n0 = qh * 32 + 8 * i4 + 4 * hi32;
+            const f32x4 L = *(const f32x4*)(l2s + n0);
+            const f32x4 Dd = *(const f32x4*)(dss + n0);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = 4 * i4 + u, n = qh * 32 + 8 * i4 + u;
-            const bool vis =
-                !need_mask || ((unsigned)(n + ba) < (unsigned)tm.la) | ((unsigned)(n + bb) < (unsigned)tm.lb);
-            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], C, -L[u])) : 0.f;
-            x[i] = p;
-            dp[i] = vis ? p * (dp[i] - Dd[u]) : 0.f;
+            for (int u = 0; u < 4; ++u) {
+              const int i = 4 * i4 + u;
+              const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], C, -L[u]));
+              x[i] = p;
+              dp[i] = p * (dp[i] - Dd[u]);
+            }
+          }
+        } else {
+          const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int n0 = qh * 32 + 8 * i4 + 4 * hi32;
+            const f32x4 L = *(const f32x4*)(l2s + n0);
+            const f32x4 Dd = *(const f32x4*)(dss + n0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int i = 4 * i4 + u, n = qh * 32 + 8 * i4 + u;
+              const bool vis = ((unsigned)(n + ba) < (unsigned)tm.la) | ((unsigned)(n + bb) < (unsigned)tm.lb);
+              const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], C, -L[u])) : 0.f;
+              x[i] = p;
+              dp[i] = vis ? p * (dp[i] - Dd[u]) : 0.f;
+            }
           }
         }
         const bf16x8 pb0 = __builtin_convertvector(x.lo, bf16x8), pb1 = __builtin_convertvector(x.hi, bf16x8);
@@ -489,17 +543,11 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
         for (int c = 0; c < NCT; ++c)
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
-            const int r0 = qh * 32 + jj * 16 + 4 * hi32 + ((lane & 15) >> 2);
-            const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            int o0 = r0 * ROW + c0, o1 = (r0 + 8) * ROW + c0;
-            if constexpr (DMA) {
-              o0 = r0 * ROW + ((((c0 >> 3) ^ swz_rt(r0)) << 3) | (c0 & 7));
-              o1 = (r0 + 8) * ROW + ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7));
-            }
-            const bf16x8 ot = __builtin_shufflevector(lds_read_tr(os + o0), lds_read_tr(os + o1), 0, 1, 2, 3, 4, 5, 6,
-                                                      7);
-            const bf16x8 qt8 = __builtin_shufflevector(lds_read_tr(qs + o0), lds_read_tr(qs + o1), 0, 1, 2, 3, 4, 5,
-                                                       6, 7);
+            const int ro = jj * 16 * ROW;
+            const bf16x8 ot = __builtin_shufflevector(lds_read_tr(qh_o + ro + tr0_off[c]),
+                                                      lds_read_tr(qh_o + ro + tr1_off[c]), 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 qt8 = __builtin_shufflevector(lds_read_tr(qh_q + ro + tr0_off[c]),
+                                                       lds_read_tr(qh_q + ro + tr1_off[c]), 0, 1, 2, 3, 4, 5, 6, 7);
             dv[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, jj ? pb1 : pb0, dv[c], 0, 0, 0);
             dk[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt8, jj ? sb1 : sb0, dk[c], 0, 0, 0);
           }

@@ -50,28 +50,31 @@ __device__ __forceinline__ int pos_of(const PartInfo& p, int owner, int i) {
   return i < half ? owner * half + i : (2 * p.cp - 1 - owner) * half + (i - half);
 }
 
-// Runs covering local indices [a, b) of `owner`; returns the number of runs (0..2).
-__device__ __forceinline__ int runs_of(const PartInfo& p, int owner, int a, int b, Run* r) {
-  if (b <= a) return 0;
+// Runs covering local indices [a, b) of `owner`, in two fixed slots (a slot
+// with cnt == 0 is empty): slot 0 holds the contiguous / striped run or the
+// part in the first zigzag half, slot 1 the part in the second zigzag half.
+// Fixed slots keep both runs in registers (no dynamically indexed array).
+__device__ __forceinline__ void runs_of(const PartInfo& p, int owner, int a, int b, Run& r0, Run& r1) {
+  r0 = Run{0, 1, 0, 0};
+  r1 = Run{0, 1, 0, 0};
+  if (b <= a) return;
   if (p.part == PART_CONTIGUOUS) {
-    r[0] = Run{owner * p.s_local + a, 1, b - a, 0};
-    return 1;
+    r0 = Run{owner * p.s_local + a, 1, b - a, 0};
+    return;
   }
   if (p.part == PART_STRIPED) {
-    r[0] = Run{owner + p.cp * a, p.cp, b - a, 0};
-    return 1;
+    r0 = Run{owner + p.cp * a, p.cp, b - a, 0};
+    return;
   }
   const int half = p.s_local >> 1;
-  int n = 0;
   if (a < half) {
     const int e = b < half ? b : half;
-    r[n++] = Run{owner * half + a, 1, e - a, 0};
+    r0 = Run{owner * half + a, 1, e - a, 0};
   }
   if (b > half) {
     const int s0 = a > half ? a : half;
-    r[n++] = Run{(2 * p.cp - 1 - owner) * half + (s0 - half), 1, b - s0, s0 - a};
+    r1 = Run{(2 * p.cp - 1 - owner) * half + (s0 - half), 1, b - s0, s0 - a};
   }
-  return n;
 }
 
 // Document containing position p: largest j with cu[j] <= p (cu has n_docs+1 entries).
@@ -167,16 +170,20 @@ __device__ inline int classify_runs(const Run& Q, const Run& K, const int* cu, i
 // Class of the tile (query rows [qa, qb) of `rank`) x (keys [ka, kb) of `owner`).
 __device__ inline int classify_tile(const PartInfo& p, int rank, int qa, int qb, int owner, int ka, int kb,
                                     const int* cu, int n_docs, int s_total, int causal) {
-  Run qr[2], kr[2];
-  const int nq = runs_of(p, rank, qa, qb, qr);
-  const int nk = runs_of(p, owner, ka, kb, kr);
+  Run q0, q1, k0, k1;
+  runs_of(p, rank, qa, qb, q0, q1);
+  runs_of(p, owner, ka, kb, k0, k1);
   bool any = false, all = true;
-  for (int i = 0; i < nq; ++i)
-    for (int j = 0; j < nk; ++j) {
-      const int c = classify_runs(qr[i], kr[j], cu, n_docs, s_total, causal);
-      any |= c != CLS_SKIP;
-      all &= c == CLS_FULL;
-    }
+  auto pair = [&](const Run& q, const Run& k) {
+    if (q.cnt <= 0 || k.cnt <= 0) return;
+    const int c = classify_runs(q, k, cu, n_docs, s_total, causal);
+    any |= c != CLS_SKIP;
+    all &= c == CLS_FULL;
+  };
+  pair(q0, k0);
+  pair(q0, k1);
+  pair(q1, k0);
+  pair(q1, k1);
   if (!any) return CLS_SKIP;
   return all ? CLS_FULL : CLS_PARTIAL;
 }

@@ -64,20 +64,21 @@ __device__ __forceinline__ TileMask tile_mask(const PartInfo& p, int owner, int 
     t.la = kb - ka;
     return t;
   }
-  Run kr[2];
-  const int nr = runs_of(p, owner, ka, kb, kr);
+  Run k0, k1;
+  runs_of(p, owner, ka, kb, k0, k1);
   int n0, n1;
-  if (nr > 0) {
-    run_range(kr[0], lo, hi, n0, n1);
-    t.i0a = kr[0].off + n0;
-    t.la = n1 >= n0 ? n1 - n0 + 1 : 0;
-  }
-  if (nr > 1) {
-    run_range(kr[1], lo, hi, n0, n1);
-    t.i0b = kr[1].off + n0;
-    t.lb = n1 >= n0 ? n1 - n0 + 1 : 0;
-  }
+  run_range(k0, lo, hi, n0, n1);  // an empty slot gives an empty interval
+  t.i0a = k0.off + n0;
+  t.la = n1 >= n0 ? n1 - n0 + 1 : 0;
+  run_range(k1, lo, hi, n0, n1);
+  t.i0b = k1.off + n0;
+  t.lb = n1 >= n0 ? n1 - n0 + 1 : 0;
   return t;
+}
+
+// True when the lane's interval set covers all n indices of the tile.
+__device__ __forceinline__ bool tile_all_visible(const TileMask& t, int n) {
+  return (t.i0a == 0 && t.la == n) || (t.i0b == 0 && t.lb == n);
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
