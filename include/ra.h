@@ -212,6 +212,42 @@ ra_status ra_classify(const ra_shape* shape, const int32_t* cu_seqlens, int32_t 
 ra_status ulysses_permute(const void* in, void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
                           int32_t elem_bytes, int32_t inverse, void* stream);
 
+/* ulysses_permute with the n blocks of the head-split side ([n s_local][h/n][d]
+ * each) placed block_stride bytes apart instead of back to back: the output of a
+ * forward permute, the input of an inverse one. This lets a Ulysses x Ring grid
+ * place device (u, r)'s head slice at [u][r], so that the ring chunks of one head
+ * slice are contiguous (see usp_forward). block_stride is a multiple of
+ * (h/n) d elem_bytes and at least n s_local (h/n) d elem_bytes; the packed side and
+ * the span of the strided side must not overlap. */
+ra_status ulysses_permute_strided(const void* in, void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
+                                  int32_t elem_bytes, int32_t inverse, int64_t block_stride, void* stream);
+
+/* Bytes of device workspace for usp_forward (head-split Q, K, V, O of the grid and
+ * one ring rank's plan). Returns 0 for an invalid shape. */
+size_t usp_workspace_size(const ra_shape* shape, int32_t ulysses, int32_t ring, int32_t n_docs);
+
+/* Hybrid Ulysses x Ring ("USP") for a grid of ulysses x ring simulated devices
+ * ([CP-TE] 2.4 and 6: Ulysses head rearrangement inside a group, Ring passing the
+ * sequence across groups; [How-to] 6; [LongCtx] timeline, USP):
+ *   the ring partition (RA_PART_*, cp = ring) splits the sequence over `ring`
+ *   groups; group r's tokens, in partition-local order, are cut into `ulysses`
+ *   equal pieces, one per device (u, r). Inside each group the Ulysses permute
+ *   gives device (u, r) the group's tokens for heads [u hq/U, (u+1) hq/U) (K, V:
+ *   [u hkv/U, (u+1) hkv/U)); device (u, r) runs ring attention (rank r of `ring`)
+ *   over the chunks of its head slice; the inverse permute returns every device
+ *   its own tokens for all heads.
+ *   q          device [ring][ulysses][S/(ring ulysses)][hq][d] in_dtype: every device's input
+ *   k, v       device [ring][ulysses][S/(ring ulysses)][hkv][d] in_dtype
+ *   out        device [ring][ulysses][S/(ring ulysses)][hq][d] out_dtype
+ *   lse        device fp32 [ulysses][ring][hq/ulysses][S/ring]: device (u, r)'s ring LSE,
+ *              in group r's partition-local token order
+ * hq % ulysses or hkv % ulysses != 0 gives RA_ERR_HEADS (the Ulysses degree is
+ * bounded by the head count, [How-to] 5); (S / ring) % ulysses != 0 gives
+ * RA_ERR_DIVISIBILITY. The whole grid runs on the caller's stream. */
+ra_status usp_forward(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_docs,
+                      int32_t ulysses, int32_t ring, int32_t partition, const ra_shape* shape, void* out,
+                      float* lse, void* workspace, size_t ws_bytes, void* stream);
+
 /* CP reorder between the global sequence and the rank-major partitioned layout:
  *   forward  in [s][h][d] (global order) -> out [cp][s/cp][h][d], out[r][i] = in[pos_r(i)]
  *   inverse  in [cp][s/cp][h][d] -> out [s][h][d]

@@ -35,6 +35,7 @@ from .attention import (attention_rows, attention_rank, step_partials, lse_merge
 from .layouts import cp_reorder, ulysses_permute
 from .classify import classify_tiles, SKIP, PARTIAL, FULL
 from .backward import attention_rows_backward, attention_rank_backward, ring_step_gradients
+from .usp import usp_device_shards, usp_forward
 
 __all__ = [
     "positions", "doc_bounds", "visible_matrix", "visible_counts",
@@ -42,4 +43,5 @@ __all__ = [
     "online_softmax_blocks", "ring_chunk_order",
     "cp_reorder", "ulysses_permute", "classify_tiles", "SKIP", "PARTIAL", "FULL",
     "attention_rows_backward", "attention_rank_backward", "ring_step_gradients",
+    "usp_device_shards", "usp_forward",
 ]

@@ -6,7 +6,8 @@ fails loudly when the library is missing; there is no fallback of any kind.
 
 Function names mirror the C entry points: ra_forward, ra_plan,
 ra_forward_planned, ra_forward_steps, ra_backward, ra_lse_merge, ra_classify,
-ulysses_permute, cp_reorder, ra_workspace_size, ra_backward_workspace_size,
+ulysses_permute, ulysses_permute_strided, usp_forward, cp_reorder,
+ra_workspace_size, ra_backward_workspace_size, usp_workspace_size,
 ra_status_string.
 """
 from __future__ import annotations
@@ -30,7 +31,8 @@ PARTITIONS = {"contiguous": 0, "zigzag": 1, "striped": 2}
 # Symbols declared in include/ra.h.
 EXPORTS = ("ra_workspace_size", "ra_forward", "ra_plan", "ra_forward_planned", "ra_forward_steps",
            "ra_backward_workspace_size", "ra_backward", "ra_lse_merge", "ra_classify",
-           "ulysses_permute", "cp_reorder", "ra_status_string", "ra_abi_version")
+           "ulysses_permute", "ulysses_permute_strided", "usp_workspace_size", "usp_forward",
+           "cp_reorder", "ra_status_string", "ra_abi_version")
 
 
 class RAError(RuntimeError):
@@ -79,6 +81,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_classify.restype = ctypes.c_int
     lib.ulysses_permute.argtypes = [vp, vp, i32, i64, i32, i32, i32, i32, vp]
     lib.ulysses_permute.restype = ctypes.c_int
+    lib.ulysses_permute_strided.argtypes = [vp, vp, i32, i64, i32, i32, i32, i32, i64, vp]
+    lib.ulysses_permute_strided.restype = ctypes.c_int
+    lib.usp_workspace_size.argtypes = [shp, i32, i32, i32]
+    lib.usp_workspace_size.restype = sz
+    lib.usp_forward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
+    lib.usp_forward.restype = ctypes.c_int
     lib.cp_reorder.argtypes = [vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.cp_reorder.restype = ctypes.c_int
     lib.ra_status_string.argtypes = [ctypes.c_int]
@@ -331,6 +339,62 @@ def ulysses_permute(x, n: int, inverse: bool = False, out=None, stream=None):
                                         int(bool(inverse)), _stream(stream))
     _check(st, "ulysses_permute")
     return out
+
+
+def ulysses_permute_strided(x, n: int, out, block_stride: int, inverse: bool = False, h: Optional[int] = None,
+                            stream=None):
+    """ulysses_permute with the head-split side's n blocks block_stride bytes apart.
+    Forward: x [n, s_l, h, d] -> blocks of out; inverse: blocks of x -> out [n, s_l, h, d].
+    `out` (forward) or `x` (inverse) is the base tensor of the strided side; for the
+    inverse pass the full head count h."""
+    if not inverse:
+        nn, s_l, hh, d = x.shape
+    else:
+        nn, s_l, hh, d = out.shape
+    if nn != n:
+        raise ValueError("leading dimension must equal n")
+    st = load_library().ulysses_permute_strided(_ptr(x), _ptr(out), int(n), int(s_l), int(hh), int(d),
+                                                x.element_size(), int(bool(inverse)), int(block_stride),
+                                                _stream(stream))
+    _check(st, "ulysses_permute_strided")
+    return out
+
+
+def usp_workspace_size(shape: ra_shape, ulysses: int, ring: int, n_docs: int = 0) -> int:
+    return int(load_library().usp_workspace_size(ctypes.byref(shape), int(ulysses), int(ring), int(n_docs)))
+
+
+def usp_forward(q, k, v, cu_seqlens=None, ulysses: int = 1, ring: int = 1, partition="contiguous", *,
+                causal: bool = True, softmax_scale: float = 0.0, out_dtype=None, out=None, lse=None, workspace=None,
+                stream=None):
+    """Ulysses x Ring grid on one GPU. q [ring, ulysses, S/(ring ulysses), hq, d]; k, v the same with hkv.
+    Returns (out [ring, ulysses, S/(ring ulysses), hq, d], lse fp32 [ulysses, ring, hq/ulysses, S/ring])."""
+    import torch
+    if q.dim() != 5 or k.dim() != 5 or v.shape != k.shape:
+        raise ValueError("q, k, v must be [ring, ulysses, S/(ring ulysses), heads, d]")
+    R, U, sh, hq, d = q.shape
+    hkv = k.shape[3]
+    if (R, U, sh) != tuple(k.shape[:3]) or R != ring or U != ulysses or k.shape[4] != d:
+        raise ValueError("q / k / v shapes disagree with the grid")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    S = R * U * sh
+    shape = make_shape(S, hq, hkv, d, causal, softmax_scale, _dtype_code(q.dtype), _dtype_code(out_dtype))
+    cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
+    if out is None:
+        out = torch.empty((R, U, sh, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((U, R, hq // max(1, U), S // R), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(256, usp_workspace_size(shape, U, R, n_docs)), dtype=torch.uint8,
+                                device=q.device)
+    st = load_library().usp_forward(_ptr(q), _ptr(k), _ptr(v), cu_ptr, n_docs, int(U), int(R), _part(partition),
+                                    ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "usp_forward")
+    return out, lse
 
 
 def cp_reorder(x, cp_size: int, partition, inverse: bool = False, out=None, stream=None):

@@ -247,8 +247,78 @@ ra_status ulysses_permute(const void* in, void* out, int32_t n, int64_t s_local,
   const ra_status s = check_ulysses(in, out, n, s_local, h, d, elem_bytes, inverse);
   if (s != RA_OK) return s;
   const int64_t run_bytes = (int64_t)(h / n) * d * elem_bytes;
-  return launch_ulysses(in, out, n, s_local, run_bytes, inverse, as_stream(stream)) == hipSuccess ? RA_OK
-                                                                                                   : RA_ERR_HIP;
+  return launch_ulysses(in, out, n, s_local, run_bytes, inverse, (int64_t)n * s_local, as_stream(stream)) ==
+                 hipSuccess
+             ? RA_OK
+             : RA_ERR_HIP;
+}
+
+ra_status ulysses_permute_strided(const void* in, void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
+                                  int32_t elem_bytes, int32_t inverse, int64_t block_stride, void* stream) {
+  const ra_status s = check_ulysses_strided(in, out, n, s_local, h, d, elem_bytes, inverse, block_stride);
+  if (s != RA_OK) return s;
+  const int64_t run_bytes = (int64_t)(h / n) * d * elem_bytes;
+  return launch_ulysses(in, out, n, s_local, run_bytes, inverse, block_stride / run_bytes, as_stream(stream)) ==
+                 hipSuccess
+             ? RA_OK
+             : RA_ERR_HIP;
+}
+
+size_t usp_workspace_size(const ra_shape* shape, int32_t ulysses, int32_t ring, int32_t n_docs) {
+  if (!shape || shape->s_total < 1 || shape->s_total > ((int64_t)1 << 30)) return 0;
+  if (ring < 1 || ring > 64 || ulysses < 1 || shape->s_total % ring) return 0;
+  if (shape->hq < 1 || shape->hkv < 1 || shape->hq % ulysses || shape->hkv % ulysses) return 0;
+  if (shape->in_dtype != RA_BF16 && shape->in_dtype != RA_F32) return 0;
+  if (shape->d < 1) return 0;
+  return usp_layout(shape, ulysses, ring, n_docs > 1 ? n_docs : 1).total;
+}
+
+ra_status usp_forward(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_docs,
+                      int32_t ulysses, int32_t ring, int32_t partition, const ra_shape* shape, void* out, float* lse,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  const ra_status s =
+      check_usp(q, k, v, cu_seqlens, n_docs, ulysses, ring, partition, shape, out, lse, workspace, ws_bytes);
+  if (s != RA_OK) return s;
+  const hipStream_t st = as_stream(stream);
+  const int32_t nd = effective_docs(cu_seqlens, n_docs);
+  const UspLayout U = usp_layout(shape, ulysses, ring, nd);
+  const int64_t S = shape->s_total, sl = S / ring, shard = sl / ulysses, d = shape->d;
+  const int64_t ei = shape->in_dtype == RA_BF16 ? 2 : 4, eo = shape->out_dtype == RA_BF16 ? 2 : 4;
+  const int64_t hq = shape->hq, hkv = shape->hkv, hqs = hq / ulysses, hkvs = hkv / ulysses;
+  char* ws = (char*)workspace;
+  char *QU = ws + U.q_off, *KU = ws + U.k_off, *VU = ws + U.v_off, *OU = ws + U.o_off;
+  void* plan = ws + U.plan_off;
+  // 1. Ulysses all-to-all inside every ring group r: device (u, r)'s head slice lands at [u][r]
+  for (int32_t r = 0; r < ring; ++r) {
+    const int64_t gq = r * ulysses * shard * hq * d * ei, gk = r * ulysses * shard * hkv * d * ei;
+    if (launch_ulysses((const char*)q + gq, QU + r * sl * hqs * d * ei, ulysses, shard, hqs * d * ei, 0,
+                       (int64_t)ring * sl, st) != hipSuccess ||
+        launch_ulysses((const char*)k + gk, KU + r * sl * hkvs * d * ei, ulysses, shard, hkvs * d * ei, 0,
+                       (int64_t)ring * sl, st) != hipSuccess ||
+        launch_ulysses((const char*)v + gk, VU + r * sl * hkvs * d * ei, ulysses, shard, hkvs * d * ei, 0,
+                       (int64_t)ring * sl, st) != hipSuccess)
+      return RA_ERR_HIP;
+  }
+  // 2. ring attention of device (u, r) over the R chunks of head slice u
+  for (int32_t r = 0; r < ring; ++r) {
+    const ra_status p = run_plan(cu_seqlens, nd, ring, r, partition, &U.slice, plan, st);
+    if (p != RA_OK) return p;
+    for (int32_t u = 0; u < ulysses; ++u) {
+      const int64_t dev = (int64_t)u * ring + r;
+      const ra_status a = run_attention(QU + dev * sl * hqs * d * ei, KU + (int64_t)u * ring * sl * hkvs * d * ei,
+                                        VU + (int64_t)u * ring * sl * hkvs * d * ei, nd, ring, r, partition, &U.slice,
+                                        OU + dev * sl * hqs * d * eo, lse + dev * hqs * sl, nullptr, nullptr, plan, st,
+                                        false);
+      if (a != RA_OK) return a;
+    }
+  }
+  // 3. inverse all-to-all inside every ring group
+  for (int32_t r = 0; r < ring; ++r) {
+    if (launch_ulysses(OU + r * sl * hqs * d * eo, (char*)out + r * ulysses * shard * hq * d * eo, ulysses, shard,
+                       hqs * d * eo, 1, (int64_t)ring * sl, st) != hipSuccess)
+      return RA_ERR_HIP;
+  }
+  return RA_OK;
 }
 
 ra_status cp_reorder(const void* in, void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes, int32_t cp_size,

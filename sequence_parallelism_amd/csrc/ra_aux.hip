@@ -242,6 +242,7 @@ struct CopyArgs {
   int s_local;    // CP reorder: tokens per rank; Ulysses: tokens per simulated rank
   int cp;         // CP reorder: cp size; Ulysses: n
   int part;
+  long long bstride;  // Ulysses: runs between the n blocks of the head-split side (n s_local if packed)
 };
 
 template <int KIND>
@@ -271,15 +272,27 @@ __device__ __forceinline__ long long src_row(const CopyArgs& c, long long R) {
     }
     return (long long)r * c.s_local + i;
   } else if constexpr (KIND == MAP_ULY_FWD) {
-    // dst run (rho, j*s_local + i) <- src run ((j*s_local + i), rho)
+    // dst run (rho, j*s_local + i) <- src run ((j*s_local + i), rho); R counts packed dst runs
     const long long T = (long long)c.cp * c.s_local;
     const long long rho = R / T, tok = R - rho * T;
     return tok * c.cp + rho;
   } else {
-    // dst run ((j*s_local + i), rho) <- src run (rho, j*s_local + i)
-    const long long T = (long long)c.cp * c.s_local;
+    // dst run ((j*s_local + i), rho) <- src run (rho, j*s_local + i), head-split blocks bstride apart
     const long long tok = R / c.cp, rho = R - tok * c.cp;
-    return rho * T + tok;
+    return rho * c.bstride + tok;
+  }
+}
+
+// Destination run of packed destination index R (the Ulysses forward writes its
+// head-split blocks bstride runs apart; every other map is packed).
+template <int KIND>
+__device__ __forceinline__ long long dst_row(const CopyArgs& c, long long R) {
+  if constexpr (KIND == MAP_ULY_FWD) {
+    const long long T = (long long)c.cp * c.s_local;
+    const long long rho = R / T;
+    return rho * c.bstride + (R - rho * T);
+  } else {
+    return R;
   }
 }
 
@@ -290,7 +303,7 @@ __global__ void __launch_bounds__(256) copy_rows_kernel(const CopyArgs c) {
   for (long long R = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); R < c.nrows; R += nw) {
     const long long S = src_row<KIND>(c, R);
     const T* src = (const T*)c.in + S * c.cpr;
-    T* dst = (T*)c.out + R * c.cpr;
+    T* dst = (T*)c.out + dst_row<KIND>(c, R) * c.cpr;
     long long i = lane;
     for (; i + 192 < c.cpr; i += 256) {
       const T a0 = src[i], a1 = src[i + 64], a2 = src[i + 128], a3 = src[i + 192];
@@ -342,7 +355,8 @@ __global__ void __launch_bounds__(256) copy_rows_pow2_kernel(const CopyArgs c, i
           const long long R = idx >> log2_cpr;
           __builtin_nontemporal_store(v[u], dst + ((src_row<KIND>(c, R) << log2_cpr) | (idx & cmask)));
         } else {
-          __builtin_nontemporal_store(v[u], dst + idx);
+          const long long R = idx >> log2_cpr;
+          __builtin_nontemporal_store(v[u], dst + ((dst_row<KIND>(c, R) << log2_cpr) | (idx & cmask)));
         }
       }
     }
@@ -351,7 +365,7 @@ __global__ void __launch_bounds__(256) copy_rows_pow2_kernel(const CopyArgs c, i
 
 template <int KIND, bool SCATTER = false>
 static hipError_t launch_copy(const void* in, void* out, long long nrows, long long row_bytes, int s_local, int cp,
-                              int part, hipStream_t st) {
+                              int part, hipStream_t st, long long bstride = 0) {
   if (nrows == 0 || row_bytes == 0) return hipSuccess;
   const uintptr_t al = (uintptr_t)in | (uintptr_t)out | (uintptr_t)row_bytes;
   const long long cpr16 = row_bytes / 16;
@@ -361,7 +375,7 @@ static hipError_t launch_copy(const void* in, void* out, long long nrows, long l
     const long long chunks = nrows * cpr16;
     long long blocks = (chunks + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
     if (blocks > 65536) blocks = 65536;
-    CopyArgs c{in, out, nrows, cpr16, s_local, cp, part};
+    CopyArgs c{in, out, nrows, cpr16, s_local, cp, part, bstride};
     hipLaunchKernelGGL((copy_rows_pow2_kernel<KIND, SCATTER>), dim3((unsigned)blocks), dim3(256), 0, st, c, lg);
     return hipGetLastError();
   }
@@ -370,19 +384,19 @@ static hipError_t launch_copy(const void* in, void* out, long long nrows, long l
   if (blocks > 4096) blocks = 4096;
   const dim3 grid((unsigned)blocks), block(256);
   if (al % 16 == 0) {
-    CopyArgs c{in, out, nrows, row_bytes / 16, s_local, cp, part};
+    CopyArgs c{in, out, nrows, row_bytes / 16, s_local, cp, part, bstride};
     hipLaunchKernelGGL((copy_rows_kernel<uint4, KIND>), grid, block, 0, st, c);
   } else if (al % 8 == 0) {
-    CopyArgs c{in, out, nrows, row_bytes / 8, s_local, cp, part};
+    CopyArgs c{in, out, nrows, row_bytes / 8, s_local, cp, part, bstride};
     hipLaunchKernelGGL((copy_rows_kernel<uint2, KIND>), grid, block, 0, st, c);
   } else if (al % 4 == 0) {
-    CopyArgs c{in, out, nrows, row_bytes / 4, s_local, cp, part};
+    CopyArgs c{in, out, nrows, row_bytes / 4, s_local, cp, part, bstride};
     hipLaunchKernelGGL((copy_rows_kernel<uint32_t, KIND>), grid, block, 0, st, c);
   } else if (al % 2 == 0) {
-    CopyArgs c{in, out, nrows, row_bytes / 2, s_local, cp, part};
+    CopyArgs c{in, out, nrows, row_bytes / 2, s_local, cp, part, bstride};
     hipLaunchKernelGGL((copy_rows_kernel<uint16_t, KIND>), grid, block, 0, st, c);
   } else {
-    CopyArgs c{in, out, nrows, row_bytes, s_local, cp, part};
+    CopyArgs c{in, out, nrows, row_bytes, s_local, cp, part, bstride};
     hipLaunchKernelGGL((copy_rows_kernel<uint8_t, KIND>), grid, block, 0, st, c);
   }
   return hipGetLastError();
@@ -396,16 +410,16 @@ hipError_t launch_cp_reorder(const void* in, void* out, int64_t s, int64_t row_b
 }
 
 hipError_t launch_ulysses(const void* in, void* out, int n, int64_t s_local, int64_t run_bytes, int inverse,
-                          hipStream_t st) {
+                          int64_t block_runs, hipStream_t st) {
   const long long runs = (long long)n * n * s_local;
-  if (inverse) return launch_copy<MAP_ULY_INV>(in, out, runs, run_bytes, (int)s_local, n, 0, st);
+  if (inverse) return launch_copy<MAP_ULY_INV>(in, out, runs, run_bytes, (int)s_local, n, 0, st, block_runs);
   // forward: walking the source in order (sequential reads, n write streams) and
   // scattering with the inverse map beats gathering 2 KB runs at an n-run stride
   const uintptr_t al = (uintptr_t)in | (uintptr_t)out | (uintptr_t)run_bytes;
   const long long cpr16 = run_bytes / 16;
   if (al % 16 == 0 && cpr16 <= 1024 && (cpr16 & (cpr16 - 1)) == 0)
-    return launch_copy<MAP_ULY_INV, true>(in, out, runs, run_bytes, (int)s_local, n, 0, st);
-  return launch_copy<MAP_ULY_FWD>(in, out, runs, run_bytes, (int)s_local, n, 0, st);
+    return launch_copy<MAP_ULY_INV, true>(in, out, runs, run_bytes, (int)s_local, n, 0, st, block_runs);
+  return launch_copy<MAP_ULY_FWD>(in, out, runs, run_bytes, (int)s_local, n, 0, st, block_runs);
 }
 
 }  // namespace ra

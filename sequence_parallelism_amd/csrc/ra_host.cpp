@@ -208,6 +208,63 @@ ra_status check_ulysses(const void* in, const void* out, int32_t n, int64_t s_lo
   return RA_OK;
 }
 
+ra_status check_ulysses_strided(const void* in, const void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
+                                int32_t elem_bytes, int32_t inverse, int64_t block_stride) {
+  if (!in || !out) return RA_ERR_NULL;
+  if (n < 1 || s_local < 1 || h < 1 || d < 1) return RA_ERR_SHAPE;
+  if (inverse != 0 && inverse != 1) return RA_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return RA_ERR_UNSUPPORTED;
+  if (h % n != 0) return RA_ERR_HEADS;
+  if ((int64_t)n * s_local > kMaxTokens) return RA_ERR_SHAPE;
+  const uint64_t bytes = (uint64_t)n * (uint64_t)s_local * (uint64_t)h * (uint64_t)d * (uint64_t)elem_bytes;
+  if (bytes > ((uint64_t)1 << 42)) return RA_ERR_SHAPE;
+  const uint64_t run = (uint64_t)(h / n) * (uint64_t)d * (uint64_t)elem_bytes;
+  const uint64_t block = bytes / (uint64_t)n;
+  if (block_stride < 0 || (uint64_t)block_stride < block || (uint64_t)block_stride % run != 0) return RA_ERR_SHAPE;
+  const uint64_t span = (uint64_t)(n - 1) * (uint64_t)block_stride + block;
+  if (span > ((uint64_t)1 << 44)) return RA_ERR_SHAPE;
+  // the packed side and the strided side must not overlap
+  const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out;
+  const uint64_t ea = inverse ? span : bytes, eb = inverse ? bytes : span;
+  if (a < b + eb && b < a + ea) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+UspLayout usp_layout(const ra_shape* shape, int32_t ulysses, int32_t ring, int32_t n_docs_dev) {
+  UspLayout U{};
+  U.slice = *shape;
+  U.slice.hq = shape->hq / ulysses;
+  U.slice.hkv = shape->hkv / ulysses;
+  const size_t ei = shape->in_dtype == RA_BF16 ? 2 : 4, eo = shape->out_dtype == RA_BF16 ? 2 : 4;
+  const size_t S = (size_t)shape->s_total, d = (size_t)shape->d;
+  U.q_off = 0;
+  U.k_off = align256(U.q_off + S * shape->hq * d * ei);
+  U.v_off = align256(U.k_off + S * shape->hkv * d * ei);
+  U.o_off = align256(U.v_off + S * shape->hkv * d * ei);
+  U.plan_off = align256(U.o_off + S * shape->hq * d * eo);
+  U.plan_bytes = attn_layout(&U.slice, ring, n_docs_dev).total;
+  U.total = align256(U.plan_off + U.plan_bytes);
+  return U;
+}
+
+ra_status check_usp(const void* q, const void* k, const void* v, const int32_t* cu, int32_t n_docs, int32_t ulysses,
+                    int32_t ring, int32_t partition, const ra_shape* shape, const void* out, const float* lse,
+                    const void* workspace, size_t ws_bytes) {
+  if (!q || !k || !v || !shape || !out || !lse) return RA_ERR_NULL;
+  if (ulysses < 1 || ulysses > kMaxHeads) return RA_ERR_SHAPE;
+  ra_status s = check_shape(shape, ring, 0, partition);
+  if (s != RA_OK) return s;
+  if (shape->hq % ulysses != 0 || shape->hkv % ulysses != 0) return RA_ERR_HEADS;
+  if ((shape->s_total / ring) % ulysses != 0) return RA_ERR_DIVISIBILITY;
+  s = check_cu(cu, n_docs, shape->s_total);
+  if (s != RA_OK) return s;
+  const UspLayout U = usp_layout(shape, ulysses, ring, effective_docs(cu, n_docs));
+  const Layout L = attn_layout(&U.slice, ring, effective_docs(cu, n_docs));
+  if ((int64_t)L.nqt * U.slice.hq > 0x7fffffffLL) return RA_ERR_SHAPE;
+  if (!workspace || ws_bytes < U.total) return RA_ERR_WORKSPACE;
+  return RA_OK;
+}
+
 ra_status check_cp_reorder(const void* in, const void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
                            int32_t cp_size, int32_t partition, int32_t inverse) {
   if (!in || !out) return RA_ERR_NULL;

@@ -72,6 +72,23 @@ ra_status check_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, 
 ra_status check_ulysses(const void* in, const void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
                         int32_t elem_bytes, int32_t inverse);
 
+// Ulysses permute with the head-split side's n blocks block_stride bytes apart.
+ra_status check_ulysses_strided(const void* in, const void* out, int32_t n, int64_t s_local, int32_t h, int32_t d,
+                                int32_t elem_bytes, int32_t inverse, int64_t block_stride);
+
+// Workspace of usp_forward: head-split Q, K, V and O of the whole grid, then one
+// ring rank's attention plan (rebuilt for every ring rank).
+struct UspLayout {
+  ra_shape slice;       // attention shape of one device's head slice
+  size_t q_off, k_off, v_off, o_off, plan_off, total;
+  size_t plan_bytes;
+};
+UspLayout usp_layout(const ra_shape* shape, int32_t ulysses, int32_t ring, int32_t n_docs_dev);
+
+ra_status check_usp(const void* q, const void* k, const void* v, const int32_t* cu, int32_t n_docs, int32_t ulysses,
+                    int32_t ring, int32_t partition, const ra_shape* shape, const void* out, const float* lse,
+                    const void* workspace, size_t ws_bytes);
+
 ra_status check_cp_reorder(const void* in, const void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
                            int32_t cp_size, int32_t partition, int32_t inverse);
 

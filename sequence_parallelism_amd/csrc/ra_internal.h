@@ -60,7 +60,9 @@ hipError_t launch_lse_merge(int64_t rows, int h, int d, const float* o_a, const 
 hipError_t launch_cp_reorder(const void* in, void* out, int64_t s, int64_t row_bytes, int cp, int part, int inverse,
                              hipStream_t st);
 
+// Ulysses permute; block_runs = runs (of run_bytes) between the n head-split blocks
+// (n * s_local when they are packed).
 hipError_t launch_ulysses(const void* in, void* out, int n, int64_t s_local, int64_t run_bytes, int inverse,
-                          hipStream_t st);
+                          int64_t block_runs, hipStream_t st);
 
 }  // namespace ra

@@ -183,3 +183,31 @@ def test_backward_validation_codes():
     assert ra.ra_backward_workspace_size(shape(s_total=0), 4, 0) == 0
     assert _lib().ra_backward_workspace_size(None, 4, 0) == 0
     assert ra.ra_backward_workspace_size(sh, 4, 50) > need
+
+
+def test_ulysses_strided_and_usp_validation():
+    lib = _lib()
+    blk = 4 * 1024 * 8 * 128 * 2  # n s_local (h/n) d elem for n=4, s_local=1024, h=32, d=128, bf16
+    assert lib.ulysses_permute_strided(P, P2, 4, 1024, 32, 128, 2, 0, blk - 2, None) == ra.RA_ERR_SHAPE  # < block
+    assert lib.ulysses_permute_strided(P, P2, 4, 1024, 32, 128, 2, 0, blk + 2, None) == ra.RA_ERR_SHAPE  # not runs
+    assert lib.ulysses_permute_strided(P, P2, 4, 1024, 30, 128, 2, 0, blk, None) == ra.RA_ERR_HEADS
+    assert lib.ulysses_permute_strided(None, P2, 4, 1024, 32, 128, 2, 0, blk, None) == ra.RA_ERR_NULL
+    # the strided span (3 * 2 blk + blk) of the output would reach the input
+    near = ctypes.c_void_p(0x100000 + 7 * blk - 16)
+    assert lib.ulysses_permute_strided(near, P, 4, 1024, 32, 128, 2, 0, 2 * blk, None) == ra.RA_ERR_SHAPE
+    sh = shape(s_total=65536, hq=32, hkv=8)
+
+    def usp(sh, U=4, R=2, part=1, ws=P, ws_bytes=1 << 40, cu=None, n_docs=0, q=P):
+        arr = None if cu is None else (ctypes.c_int32 * len(cu))(*cu)
+        return lib.usp_forward(q, P, P, arr, n_docs, U, R, part, ctypes.byref(sh), P, P, ws, ws_bytes, None)
+
+    assert usp(sh, q=None) == ra.RA_ERR_NULL
+    assert usp(sh, U=16) == ra.RA_ERR_HEADS        # 8 KV heads cannot split 16 ways
+    assert usp(sh, U=3) == ra.RA_ERR_HEADS
+    assert usp(shape(s_total=4 * 1001, hq=4, hkv=4), U=4, R=2, part=0) == ra.RA_ERR_DIVISIBILITY  # 2002 % 4 != 0
+    assert usp(sh, R=0) == ra.RA_ERR_SHAPE
+    assert usp(sh, U=0) == ra.RA_ERR_SHAPE
+    need = ra.usp_workspace_size(sh, 4, 2, 0)
+    assert need > 0
+    assert usp(sh, ws_bytes=need - 1) == ra.RA_ERR_WORKSPACE
+    assert ra.usp_workspace_size(sh, 3, 2, 0) == 0
