@@ -84,8 +84,27 @@ typedef enum {
  *   RA_PART_ZIGZAG      S is cut into 2 cp equal chunks; rank r holds chunk r
  *                       then chunk 2 cp - 1 - r  ([LongCtx] timeline, zigzag)
  *   RA_PART_STRIPED     rank r holds positions r, r + cp, r + 2 cp, ...
- *                       ([LongCtx] timeline, Striped Attention)              */
-typedef enum { RA_PART_CONTIGUOUS = 0, RA_PART_ZIGZAG = 1, RA_PART_STRIPED = 2 } ra_partition;
+ *                       ([LongCtx] timeline, Striped Attention)
+ *   RA_PART_DOC_ZIGZAG  per-document zigzag for packed documents ([How-to] 2:
+ *                       variable lengths magnify Ring's imbalance; [LongCtx]
+ *                       timeline, dynamic CP): every document (cu_seqlens; NULL
+ *                       = one document) is cut into 2 cp contiguous pieces of
+ *                       floor(L/2cp) or one more tokens (the first L mod 2cp
+ *                       pieces get the extra one), each padded at its end to
+ *                       64 ceil(ceil(L/2cp)/64) slots; rank r holds, document
+ *                       after document, piece r then piece 2 cp - 1 - r. Padding
+ *                       slots see nothing and are seen by nothing (their O = 0,
+ *                       LSE = -inf, gradients 0). S_l is then ra_local_length()
+ *                       (> S / cp); S need not divide by cp. Accepted by
+ *                       ra_forward, ra_forward_steps, ra_backward and ra_classify
+ *                       (tiles 16, 32, 64 or 128); cp_reorder_docs moves data in
+ *                       and out of this layout.                              */
+typedef enum {
+  RA_PART_CONTIGUOUS = 0,
+  RA_PART_ZIGZAG = 1,
+  RA_PART_STRIPED = 2,
+  RA_PART_DOC_ZIGZAG = 3
+} ra_partition;
 
 typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype;
 
@@ -101,10 +120,20 @@ typedef struct {
   int32_t out_dtype;    /* ra_dtype of out: RA_BF16 or RA_F32 (RA_F32 inputs: RA_F32)  */
 } ra_shape;
 
-/* Bytes of device workspace that ra_forward / ra_forward_steps / ra_classify
- * need for this shape, CP size and document count (n_docs = 0 or 1: a single
- * document). Returns 0 for an invalid shape. */
+/* Bytes of device workspace that ra_forward / ra_forward_steps / ra_plan need for
+ * this shape, CP size and document count (n_docs = 0 or 1: a single document),
+ * for every partition. Returns 0 for an invalid shape. */
 size_t ra_workspace_size(const ra_shape* shape, int32_t cp_size, int32_t n_docs);
+
+/* Tokens (slots) one rank holds: S / cp, or for RA_PART_DOC_ZIGZAG the padded
+ * per-document pieces. cu_seqlens is a HOST array (NULL: one document). Returns
+ * -1 for invalid arguments (including S not divisible as the partition needs). */
+int64_t ra_local_length(int64_t s_total, int32_t cp_size, int32_t partition, const int32_t* cu_seqlens,
+                        int32_t n_docs);
+
+/* Bytes of device workspace that cp_reorder_docs, and ra_classify with
+ * RA_PART_DOC_ZIGZAG, need (the document tables). 0 for invalid arguments. */
+size_t ra_doc_workspace_size(int64_t s_total, int32_t cp_size, const int32_t* cu_seqlens, int32_t n_docs);
 
 /* One rank's ring attention, steps merged ([SP-concept] "Ring Attention 的不同
  * 思路" and 二; [CP-TE] 2.2 and 3.3).
@@ -122,7 +151,8 @@ ra_status ra_forward(const void* q, const void* k, const void* v, const int32_t*
                      const ra_shape* shape, void* out, float* lse, void* workspace, size_t ws_bytes,
                      void* stream);
 
-/* Planning half of ra_forward: uploads cu_seqlens and builds, in `workspace`,
+/* Planning half of ra_forward (not for RA_PART_DOC_ZIGZAG, whose local length
+ * ra_forward_planned could not know): uploads cu_seqlens and builds, in `workspace`,
  * the per-query-tile work list of non-SKIP (ring step, key tile) pairs with
  * their FULL / PARTIAL class ([CP-TE] 3.3) and the heaviest-first tile order.
  * A plan depends only on (shape, cu_seqlens, cp_size, rank, partition), so
@@ -196,7 +226,9 @@ ra_status ra_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, con
  *   0 SKIP (no visible pair), 1 PARTIAL, 2 FULL (every pair visible).
  *   cls        device int8 [cp][ceil(S_l / bm)][ceil(S_l / bn)]
  * shape supplies s_total and causal (heads and dtypes are not used).
- * bm, bn in [1, 65536]. */
+ * bm, bn in [1, 65536]; RA_PART_DOC_ZIGZAG: bm, bn in {16, 32, 64, 128}, the
+ * grid is over S_l = ra_local_length(), a tile holding padding is never FULL,
+ * and the workspace must hold ra_doc_workspace_size() bytes. */
 ra_status ra_classify(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size,
                       int32_t rank, int32_t partition, int32_t bm, int32_t bn, int8_t* cls, void* workspace,
                       size_t ws_bytes, void* stream);
@@ -248,7 +280,18 @@ ra_status usp_forward(const void* q, const void* k, const void* v, const int32_t
                       int32_t ulysses, int32_t ring, int32_t partition, const ra_shape* shape, void* out,
                       float* lse, void* workspace, size_t ws_bytes, void* stream);
 
-/* CP reorder between the global sequence and the rank-major partitioned layout:
+/* CP reorder for RA_PART_DOC_ZIGZAG:
+ *   forward  in [s][h][d] (global order) -> out [cp][S_l][h][d], padding slots zero
+ *   inverse  in [cp][S_l][h][d] -> out [s][h][d] (padding slots dropped)
+ * S_l = ra_local_length(s, cp, RA_PART_DOC_ZIGZAG, cu_seqlens, n_docs); cu_seqlens
+ * is a HOST array (NULL: one document); workspace of ra_doc_workspace_size()
+ * bytes. Bit-exact copy; in and out must not overlap. */
+ra_status cp_reorder_docs(const void* in, void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
+                          int32_t cp_size, const int32_t* cu_seqlens, int32_t n_docs, int32_t inverse,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* CP reorder between the global sequence and the rank-major partitioned layout
+ * (contiguous, zigzag, striped; RA_PART_DOC_ZIGZAG uses cp_reorder_docs):
  *   forward  in [s][h][d] (global order) -> out [cp][s/cp][h][d], out[r][i] = in[pos_r(i)]
  *   inverse  in [cp][s/cp][h][d] -> out [s][h][d]
  * pos_r from `partition` (RA_PART_*). Bit-exact copy; in and out must not overlap. */

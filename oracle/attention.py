@@ -88,8 +88,8 @@ def attention_rows(q_rows, pos_q, k_rows, v_rows, pos_k, cu_seqlens, s_total, ca
     return O, LSE
 
 
-def _rank_rows(s_total, cp, rank, partition, rows):
-    pos_q = positions(partition, s_total, cp, rank)
+def _rank_rows(s_total, cp, rank, partition, rows, cu_seqlens=None):
+    pos_q = positions(partition, s_total, cp, rank, cu_seqlens)
     if rows is not None:
         pos_q = pos_q[np.asarray(rows, dtype=np.int64)]
     return pos_q
@@ -100,9 +100,9 @@ def attention_rank(gq, gk, gv, cu_seqlens, cp, rank, partition, causal=True, sca
     sequence. gq [S, hq, d], gk/gv [S, hkv, d] in global order (fp64).
     `rows` optionally selects local row indices. Returns (O [R,hq,d], LSE [hq,R])."""
     S = gq.shape[0]
-    pos_q = _rank_rows(S, cp, rank, partition, rows)
+    pos_q = _rank_rows(S, cp, rank, partition, rows, cu_seqlens)
     pos_k = np.arange(S, dtype=np.int64)
-    return attention_rows(gq[pos_q], pos_q, gk, gv, pos_k, cu_seqlens, S, causal, scale)
+    return attention_rows(gq[np.maximum(pos_q, 0)], pos_q, gk, gv, pos_k, cu_seqlens, S, causal, scale)
 
 
 def step_partials(gq, gk, gv, cu_seqlens, cp, rank, partition, causal=True, scale=None, rows=None):
@@ -110,12 +110,13 @@ def step_partials(gq, gk, gv, cu_seqlens, cp, rank, partition, causal=True, scal
     (chunk_owner, O_t [R,hq,d], LSE_t [hq,R]), attention restricted to the keys of
     the chunk visited at step t."""
     S = gq.shape[0]
-    pos_q = _rank_rows(S, cp, rank, partition, rows)
-    q_rows = gq[pos_q]
+    pos_q = _rank_rows(S, cp, rank, partition, rows, cu_seqlens)
+    q_rows = gq[np.maximum(pos_q, 0)]
     out = []
     for s in ring_chunk_order(cp, rank):
-        pos_k = positions(partition, S, cp, s)
-        O_t, L_t = attention_rows(q_rows, pos_q, gk[pos_k], gv[pos_k], pos_k, cu_seqlens, S, causal, scale)
+        pos_k = positions(partition, S, cp, s, cu_seqlens)
+        kk = np.maximum(pos_k, 0)
+        O_t, L_t = attention_rows(q_rows, pos_q, gk[kk], gv[kk], pos_k, cu_seqlens, S, causal, scale)
         out.append((s, O_t, L_t))
     return out
 

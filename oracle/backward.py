@@ -93,9 +93,10 @@ def attention_rank_backward(gq, gk, gv, dout, cu_seqlens, cp, rank, partition, c
     rank's local row order. Returns dq [S_l, hq, d] (local order) and this
     rank's contributions dk, dv [S, hkv, d] in GLOBAL order."""
     S = gq.shape[0]
-    pos_q = positions(partition, S, cp, rank)
+    pos_q = positions(partition, S, cp, rank, cu_seqlens)
     pos_k = np.arange(S, dtype=np.int64)
-    return attention_rows_backward(gq[pos_q], pos_q, gk, gv, pos_k, dout, cu_seqlens, S, causal, scale)
+    return attention_rows_backward(gq[np.maximum(pos_q, 0)], pos_q, gk, gv, pos_k, dout, cu_seqlens, S, causal,
+                                   scale)
 
 
 def ring_step_gradients(gq, gk, gv, dout, cu_seqlens, cp, rank, partition, causal=True, scale=None):
@@ -104,9 +105,9 @@ def ring_step_gradients(gq, gk, gv, dout, cu_seqlens, cp, rank, partition, causa
     (rank - t) mod CP is the chunk visited at step t and dk_t / dv_t are in that
     chunk's local order. Probabilities use the row's softmax over all steps."""
     S = gq.shape[0]
-    pos_q = positions(partition, S, cp, rank)
+    pos_q = positions(partition, S, cp, rank, cu_seqlens)
     pos_k = np.arange(S, dtype=np.int64)
-    q_rows = np.asarray(gq[pos_q], dtype=np.float64)
+    q_rows = np.asarray(gq[np.maximum(pos_q, 0)], dtype=np.float64)
     k_all = np.asarray(gk, dtype=np.float64)
     v_all = np.asarray(gv, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
@@ -116,7 +117,7 @@ def ring_step_gradients(gq, gk, gv, dout, cu_seqlens, cp, rank, partition, causa
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     order = ring_chunk_order(cp, rank)
-    chunk_pos = [positions(partition, S, cp, s) for s in order]
+    chunk_pos = [positions(partition, S, cp, s, cu_seqlens) for s in order]
     out = [(s, np.zeros((R, hq, d)), np.zeros((len(p), hkv, d)), np.zeros((len(p), hkv, d)))
            for s, p in zip(order, chunk_pos)]
     for r0, r1 in _row_blocks(R, S, budget=1 << 24):

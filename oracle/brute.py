@@ -14,9 +14,22 @@ from __future__ import annotations
 import math
 
 
-def brute_positions(partition, S, cp, r):
+def brute_positions(partition, S, cp, r, cu=None, align=64):
+    """Positions of rank r in local order; None marks doc_zigzag padding."""
     out = []
     sl = S // cp
+    if partition == "doc_zigzag":
+        bounds = cu if cu is not None else [0, S]
+        n = 2 * cp
+        for j in range(len(bounds) - 1):
+            L = bounds[j + 1] - bounds[j]
+            sizes = [L // n + (1 if k < L % n else 0) for k in range(n)]
+            slots = align * ((max(sizes) + align - 1) // align)
+            for k in (r, n - 1 - r):
+                first = bounds[j] + sum(sizes[:k])
+                for i in range(slots):
+                    out.append(first + i if i < sizes[k] else None)
+        return out
     if partition == "contiguous":
         for i in range(sl):
             out.append(r * sl + i)
@@ -51,10 +64,12 @@ def brute_attention_rank(q, k, v, cu, cp, r, partition, causal=True, scale=None)
     d = len(q[0][0])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    pos = brute_positions(partition, S, cp, r)
+    pos = brute_positions(partition, S, cp, r, cu)
     O = [[[0.0] * d for _ in range(hq)] for _ in pos]
     LSE = [[-math.inf] * len(pos) for _ in range(hq)]
     for i, pq in enumerate(pos):
+        if pq is None:
+            continue
         for h in range(hq):
             g = (h * hkv) // hq
             keys = []
@@ -84,14 +99,14 @@ def brute_attention_rank(q, k, v, cu, cp, r, partition, causal=True, scale=None)
 
 def brute_classify(S, cp, r, partition, cu, bm, bn, causal=True):
     """Nested list [CP][nqt][nkt] of 0/1/2 (skip/partial/full), by counting pairs."""
-    pos_q = brute_positions(partition, S, cp, r)
-    sl = S // cp
+    pos_q = brute_positions(partition, S, cp, r, cu)
+    sl = len(pos_q)
     nqt = (sl + bm - 1) // bm
     nkt = (sl + bn - 1) // bn
     out = []
     for t in range(cp):
         s = (r - t) % cp
-        pos_k = brute_positions(partition, S, cp, s)
+        pos_k = brute_positions(partition, S, cp, s, cu)
         grid = []
         for I in range(nqt):
             row = []
@@ -102,7 +117,8 @@ def brute_classify(S, cp, r, partition, cu, bm, bn, causal=True):
                     for j in range(J * bn, min(sl, (J + 1) * bn)):
                         n_all += 1
                         pq, pk = pos_q[i], pos_k[j]
-                        ok = (not causal or pk <= pq) and brute_doc_of(pq, cu) == brute_doc_of(pk, cu)
+                        ok = (pq is not None and pk is not None and (not causal or pk <= pq)
+                              and brute_doc_of(pq, cu) == brute_doc_of(pk, cu))
                         n_vis += 1 if ok else 0
                 row.append(0 if n_vis == 0 else (2 if n_vis == n_all else 1))
             grid.append(row)

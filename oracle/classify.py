@@ -13,7 +13,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import ring_chunk_order
-from .partition import positions, visible_matrix
+from .partition import local_length, positions, visible_matrix
 
 SKIP, PARTIAL, FULL = 0, 1, 2
 
@@ -21,15 +21,15 @@ SKIP, PARTIAL, FULL = 0, 1, 2
 def classify_tiles(s_total, cp, rank, partition, cu_seqlens, bm, bn, causal=True, return_counts=False):
     """int8 [CP, ceil(S_l/bm), ceil(S_l/bn)] tile classes (and, optionally, the
     int64 visible-pair counts per tile)."""
-    sl = s_total // cp
+    sl = local_length(partition, s_total, cp, cu_seqlens)
     nqt = -(-sl // bm)
     nkt = -(-sl // bn)
-    pos_q = positions(partition, s_total, cp, rank)
+    pos_q = positions(partition, s_total, cp, rank, cu_seqlens)
     cls = np.zeros((cp, nqt, nkt), dtype=np.int8)
     counts = np.zeros((cp, nqt, nkt), dtype=np.int64)
     kt_starts = np.arange(0, sl, bn)
     for t, s in enumerate(ring_chunk_order(cp, rank)):
-        pos_k = positions(partition, s_total, cp, s)
+        pos_k = positions(partition, s_total, cp, s, cu_seqlens)
         for I in range(nqt):
             r0, r1 = I * bm, min(sl, (I + 1) * bm)
             vis = visible_matrix(pos_q[r0:r1], pos_k, cu_seqlens, s_total, causal)

@@ -21,19 +21,28 @@ import numpy as np
 from .partition import positions
 
 
-def cp_reorder(x, cp: int, partition: str, inverse: bool = False):
-    """Forward: x [S, ...] -> [CP, S/CP, ...]. Inverse: [CP, S/CP, ...] -> [S, ...]."""
+def cp_reorder(x, cp: int, partition: str, inverse: bool = False, cu_seqlens=None, s_total=None):
+    """Forward: x [S, ...] -> [CP, S_l, ...]. Inverse: [CP, S_l, ...] -> [S, ...].
+    doc_zigzag (needs cu_seqlens; the inverse also s_total): padding rows of the
+    forward output are zero, and the inverse drops them."""
     x = np.asarray(x)
     if not inverse:
         S = x.shape[0]
-        return np.stack([x[positions(partition, S, cp, r)] for r in range(cp)])
+        rows = []
+        for r in range(cp):
+            pos = positions(partition, S, cp, r, cu_seqlens)
+            g = x[np.maximum(pos, 0)].copy()
+            g[pos < 0] = 0
+            rows.append(g)
+        return np.stack(rows)
     cpx, sl = x.shape[0], x.shape[1]
     if cpx != cp:
         raise ValueError("leading axis must equal CP")
-    S = cp * sl
+    S = cp * sl if s_total is None else s_total
     out = np.empty((S,) + x.shape[2:], dtype=x.dtype)
     for r in range(cp):
-        out[positions(partition, S, cp, r)] = x[r]
+        pos = positions(partition, S, cp, r, cu_seqlens)
+        out[pos[pos >= 0]] = x[r][pos >= 0]
     return out
 
 

@@ -12,6 +12,19 @@ positions(): which global token positions a CP rank holds, in its local order.
   striped    -- [LongCtx] timeline (Striped Attention: striped reorder fixes
                 the causal imbalance of Ring). Reading: rank r holds positions
                 r, r+CP, r+2CP, ... in increasing order. Needs S % CP == 0.
+  doc_zigzag -- per-document zigzag for packed documents. [How-to] section 2
+                notes that variable lengths magnify Ring's load imbalance (and
+                that ring-flash-attention adds balancing and variable-length
+                handling), and [LongCtx]'s timeline names dynamic CP for it,
+                without a layout. Reading: every document j (length L_j, from
+                cu_seqlens) is cut into 2*CP contiguous pieces of floor(L_j/2CP)
+                or one more tokens (the first L_j mod 2CP pieces get the extra
+                one), each padded at its end to P_j = A * ceil(ceil(L_j/2CP)/A)
+                slots, A = 64; rank r holds, document after document, piece r
+                and then piece 2*CP-1-r. Padding slots have position -1: they
+                see nothing and nothing sees them. Every rank holds sum_j 2 P_j
+                slots, and every document's causal work splits evenly, as zigzag
+                does for one sequence.
 
 Documents: cu_seqlens [n_docs+1] are packed-document offsets ([XTuner-09]
 section 9.5): tokens of different documents must not attend to each other.
@@ -25,8 +38,44 @@ from __future__ import annotations
 import numpy as np
 
 
-def positions(partition: str, s_total: int, cp: int, rank: int) -> np.ndarray:
-    """Global positions held by `rank`, in its local order (int64 [S/CP])."""
+PIECE_ALIGN = 64  # doc_zigzag pieces are padded to a multiple of this many tokens
+
+
+def doc_zigzag_piece_lengths(cu_seqlens, s_total: int, cp: int, align: int = PIECE_ALIGN) -> np.ndarray:
+    """Padded piece length P_j (slots) of every document under doc_zigzag."""
+    cu = np.asarray([0, s_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    L = cu[1:] - cu[:-1]
+    longest = -(-L // (2 * cp))
+    return align * (-(-longest // align))
+
+
+def doc_zigzag_piece_bounds(L: int, cp: int) -> np.ndarray:
+    """Document-relative start of each of the 2*CP pieces, plus the end [2*CP+1]."""
+    n = 2 * cp
+    k = np.arange(n + 1, dtype=np.int64)
+    return k * (L // n) + np.minimum(k, L % n)
+
+
+def local_length(partition: str, s_total: int, cp: int, cu_seqlens=None) -> int:
+    """Tokens each rank holds (padding included for doc_zigzag)."""
+    if partition == "doc_zigzag":
+        return int(2 * doc_zigzag_piece_lengths(cu_seqlens, s_total, cp).sum())
+    return s_total // cp
+
+
+def positions(partition: str, s_total: int, cp: int, rank: int, cu_seqlens=None) -> np.ndarray:
+    """Global positions held by `rank`, in its local order (int64 [S_l]; -1 marks
+    doc_zigzag padding)."""
+    if partition == "doc_zigzag":
+        cu = np.asarray([0, s_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+        P = doc_zigzag_piece_lengths(cu, s_total, cp)
+        out = []
+        for j in range(len(cu) - 1):
+            b = doc_zigzag_piece_bounds(int(cu[j + 1] - cu[j]), cp)
+            for piece in (rank, 2 * cp - 1 - rank):
+                i = np.arange(P[j], dtype=np.int64)
+                out.append(np.where(i < b[piece + 1] - b[piece], cu[j] + b[piece] + i, -1))
+        return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
     if partition == "contiguous":
         if s_total % cp:
             raise ValueError("S must be divisible by CP")
@@ -62,20 +111,23 @@ def doc_bounds(cu_seqlens, s_total: int):
 
 
 def visible_matrix(pos_q: np.ndarray, pos_k: np.ndarray, cu_seqlens, s_total: int, causal: bool) -> np.ndarray:
-    """Boolean [len(pos_q), len(pos_k)]: vis(pq, pk) as defined above."""
+    """Boolean [len(pos_q), len(pos_k)]: vis(pq, pk) as defined above (a padding
+    position -1 on either side is never visible)."""
     start, _ = doc_bounds(cu_seqlens, s_total)
     pq = np.asarray(pos_q, dtype=np.int64)[:, None]
     pk = np.asarray(pos_k, dtype=np.int64)[None, :]
-    same_doc = start[pq] == start[pk]
+    valid = (pq >= 0) & (pk >= 0)
+    same_doc = valid & (start[np.maximum(pq, 0)] == start[np.maximum(pk, 0)])
     if causal:
         return same_doc & (pk <= pq)
     return same_doc
 
 
 def visible_counts(pos_q: np.ndarray, cu_seqlens, s_total: int, causal: bool) -> np.ndarray:
-    """Number of visible keys (over the whole sequence) for each query position."""
+    """Number of visible keys (over the whole sequence) for each query position
+    (0 for padding)."""
     start, end = doc_bounds(cu_seqlens, s_total)
     pq = np.asarray(pos_q, dtype=np.int64)
-    if causal:
-        return pq - start[pq] + 1
-    return end[pq] - start[pq]
+    p = np.maximum(pq, 0)
+    n = (p - start[p] + 1) if causal else (end[p] - start[p])
+    return np.where(pq >= 0, n, 0)

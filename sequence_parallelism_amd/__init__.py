@@ -7,8 +7,8 @@ fails loudly when the library is missing; there is no fallback of any kind.
 Function names mirror the C entry points: ra_forward, ra_plan,
 ra_forward_planned, ra_forward_steps, ra_backward, ra_lse_merge, ra_classify,
 ulysses_permute, ulysses_permute_strided, usp_forward, cp_reorder,
-ra_workspace_size, ra_backward_workspace_size, usp_workspace_size,
-ra_status_string.
+cp_reorder_docs, ra_local_length, ra_workspace_size, ra_backward_workspace_size,
+ra_doc_workspace_size, usp_workspace_size, ra_status_string.
 """
 from __future__ import annotations
 
@@ -26,13 +26,14 @@ RA_OK = 0
 RA_ERR_NULL, RA_ERR_SHAPE, RA_ERR_DIVISIBILITY, RA_ERR_HEADS = 1, 2, 3, 4
 RA_ERR_CU_SEQLENS, RA_ERR_RANK, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = 5, 6, 7, 8, 9
 RA_BF16, RA_F32 = 0, 1
-PARTITIONS = {"contiguous": 0, "zigzag": 1, "striped": 2}
+PARTITIONS = {"contiguous": 0, "zigzag": 1, "striped": 2, "doc_zigzag": 3}
 
 # Symbols declared in include/ra.h.
 EXPORTS = ("ra_workspace_size", "ra_forward", "ra_plan", "ra_forward_planned", "ra_forward_steps",
            "ra_backward_workspace_size", "ra_backward", "ra_lse_merge", "ra_classify",
            "ulysses_permute", "ulysses_permute_strided", "usp_workspace_size", "usp_forward",
-           "cp_reorder", "ra_status_string", "ra_abi_version")
+           "cp_reorder", "cp_reorder_docs", "ra_local_length", "ra_doc_workspace_size",
+           "ra_status_string", "ra_abi_version")
 
 
 class RAError(RuntimeError):
@@ -87,6 +88,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.usp_workspace_size.restype = sz
     lib.usp_forward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
     lib.usp_forward.restype = ctypes.c_int
+    lib.ra_local_length.argtypes = [i64, i32, i32, vp, i32]
+    lib.ra_local_length.restype = i64
+    lib.ra_doc_workspace_size.argtypes = [i64, i32, vp, i32]
+    lib.ra_doc_workspace_size.restype = sz
+    lib.cp_reorder_docs.argtypes = [vp, vp, i64, i32, i32, i32, i32, vp, i32, i32, vp, sz, vp]
+    lib.cp_reorder_docs.restype = ctypes.c_int
     lib.cp_reorder.argtypes = [vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     lib.cp_reorder.restype = ctypes.c_int
     lib.ra_status_string.argtypes = [ctypes.c_int]
@@ -149,7 +156,19 @@ def ra_workspace_size(shape: ra_shape, cp_size: int, n_docs: int = 0) -> int:
     return int(load_library().ra_workspace_size(ctypes.byref(shape), int(cp_size), int(n_docs)))
 
 
-def _attn_common(q, k, v, cp_size, causal, softmax_scale, out_dtype):
+def _global_len(partition, cp, s_l, cu_seqlens, s_total):
+    """S: given, or the last cu_seqlens entry (doc_zigzag), or cp * S_l."""
+    if s_total is not None:
+        return int(s_total)
+    if _part(partition) == PARTITIONS["doc_zigzag"]:
+        if cu_seqlens is None:
+            raise ValueError("doc_zigzag needs cu_seqlens or s_total")
+        return int(np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens)[-1])
+    return cp * s_l
+
+
+def _attn_common(q, k, v, cp_size, causal, softmax_scale, out_dtype, partition="contiguous", cu_seqlens=None,
+                 s_total=None):
     if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q must be [S_l, hq, d]; k, v must be [cp, S_l, hkv, d]")
     s_l, hq, d = q.shape
@@ -162,7 +181,8 @@ def _attn_common(q, k, v, cp_size, causal, softmax_scale, out_dtype):
     in_code = _dtype_code(q.dtype)
     if out_dtype is None:
         out_dtype = q.dtype
-    shape = make_shape(cp * s_l, hq, hkv, d, causal, softmax_scale, in_code, _dtype_code(out_dtype))
+    S = _global_len(partition, cp, s_l, cu_seqlens, s_total)
+    shape = make_shape(S, hq, hkv, d, causal, softmax_scale, in_code, _dtype_code(out_dtype))
     return shape, s_l, hq, d, out_dtype
 
 
@@ -176,11 +196,12 @@ def _workspace(shape, cp_size, n_docs, device, workspace):
 
 def ra_forward(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partition="contiguous", *,
                causal: bool = True, softmax_scale: float = 0.0, out_dtype=None, out=None, lse=None,
-               workspace=None, stream=None):
+               workspace=None, stream=None, s_total=None):
     """One rank's ring attention. q [S_l,hq,d]; k, v [cp,S_l,hkv,d] (rank-major chunks).
     Returns (out [S_l,hq,d], lse fp32 [hq,S_l])."""
     import torch
-    shape, s_l, hq, d, out_dtype = _attn_common(q, k, v, cp_size, causal, softmax_scale, out_dtype)
+    shape, s_l, hq, d, out_dtype = _attn_common(q, k, v, cp_size, causal, softmax_scale, out_dtype, partition,
+                                                cu_seqlens, s_total)
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
     if out is None:
         out = torch.empty((s_l, hq, d), dtype=out_dtype, device=q.device)
@@ -236,10 +257,11 @@ def ra_forward_planned(q, k, v, plan: Plan, *, out=None, lse=None, stream=None):
 
 def ra_forward_steps(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partition="contiguous", *,
                      causal: bool = True, softmax_scale: float = 0.0, o_steps=None, lse_steps=None,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, s_total=None):
     """Per-step normalised partials: (o_steps fp32 [cp,S_l,hq,d], lse_steps fp32 [cp,hq,S_l])."""
     import torch
-    shape, s_l, hq, d, _ = _attn_common(q, k, v, cp_size, causal, softmax_scale, torch.float32)
+    shape, s_l, hq, d, _ = _attn_common(q, k, v, cp_size, causal, softmax_scale, torch.float32, partition,
+                                        cu_seqlens, s_total)
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
     if o_steps is None:
         o_steps = torch.empty((cp_size, s_l, hq, d), dtype=torch.float32, device=q.device)
@@ -259,13 +281,14 @@ def ra_backward_workspace_size(shape: ra_shape, cp_size: int, n_docs: int = 0) -
 
 def ra_backward(q, k, v, out, lse, dout, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partition="contiguous",
                 *, causal: bool = True, softmax_scale: float = 0.0, dq=None, dk=None, dv=None, workspace=None,
-                stream=None):
+                stream=None, s_total=None):
     """Gradients of one rank's ring attention. q, dout [S_l,hq,d] (input dtype); k, v
     [cp,S_l,hkv,d]; out [S_l,hq,d] and lse fp32 [hq,S_l] from the forward. Returns
     (dq fp32 [S_l,hq,d], dk fp32 [cp,S_l,hkv,d], dv fp32 [cp,S_l,hkv,d]): dk / dv hold
     this rank's contribution to every chunk's gradient."""
     import torch
-    shape, s_l, hq, d, _ = _attn_common(q, k, v, cp_size, causal, softmax_scale, out.dtype)
+    shape, s_l, hq, d, _ = _attn_common(q, k, v, cp_size, causal, softmax_scale, out.dtype, partition, cu_seqlens,
+                                        s_total)
     if dout.shape != q.shape or dout.dtype != q.dtype or out.shape != q.shape or lse.shape != (hq, s_l):
         raise ValueError("out / dout must be [S_l,hq,d] (dout in q's dtype), lse [hq,S_l]")
     for t in (out, lse, dout):
@@ -304,15 +327,56 @@ def ra_lse_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
     return o_out, lse_out
 
 
+def ra_local_length(s_total: int, cp_size: int, partition, cu_seqlens=None) -> int:
+    """Tokens (slots) one rank holds; -1 for invalid arguments."""
+    cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
+    return int(load_library().ra_local_length(int(s_total), int(cp_size), _part(partition), cu_ptr, n_docs))
+
+
+def ra_doc_workspace_size(s_total: int, cp_size: int, cu_seqlens=None) -> int:
+    cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
+    return int(load_library().ra_doc_workspace_size(int(s_total), int(cp_size), cu_ptr, n_docs))
+
+
+def cp_reorder_docs(x, cp_size: int, cu_seqlens=None, inverse: bool = False, out=None, s_total=None,
+                    workspace=None, stream=None):
+    """Per-document zigzag reorder. Forward: [S, h, d] -> [cp, S_l, h, d] (padding zero);
+    inverse: [cp, S_l, h, d] -> [S, h, d] (pass s_total when cu_seqlens is None)."""
+    import torch
+    if not x.is_contiguous():
+        raise ValueError("input must be contiguous")
+    cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
+    if not inverse:
+        s, h, d = x.shape
+    else:
+        _, _, h, d = x.shape
+        s = int(cu_arr[-1]) if cu_arr is not None else int(s_total)
+    sl = ra_local_length(s, cp_size, "doc_zigzag", cu_seqlens)
+    if out is None:
+        shape_out = (s, h, d) if inverse else (cp_size, sl, h, d)
+        out = torch.empty(shape_out, dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(256, ra_doc_workspace_size(s, cp_size, cu_seqlens)), dtype=torch.uint8,
+                                device=x.device)
+    st = load_library().cp_reorder_docs(_ptr(x), _ptr(out), int(s), int(h), int(d), x.element_size(), int(cp_size),
+                                        cu_ptr, n_docs, int(bool(inverse)), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "cp_reorder_docs")
+    return out
+
+
 def ra_classify(s_total: int, cp_size: int, rank: int, partition, bm: int, bn: int, cu_seqlens=None,
                 causal: bool = True, device="cuda", stream=None):
     """Tile classes int8 [cp, ceil(S_l/bm), ceil(S_l/bn)]: 0 skip, 1 partial, 2 full."""
     import torch
     shape = make_shape(s_total, 1, 1, 64, causal)
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
-    s_l = s_total // cp_size
+    s_l = ra_local_length(s_total, cp_size, partition, cu_seqlens)
+    if s_l < 0:
+        s_l = s_total // cp_size  # invalid arguments: the call below reports the status
     cls = torch.empty((cp_size, -(-s_l // bm), -(-s_l // bn)), dtype=torch.int8, device=device)
-    ws = torch.empty(max(256, 4 * (n_docs + 1)), dtype=torch.uint8, device=device)
+    need = ra_doc_workspace_size(s_total, cp_size, cu_seqlens) if _part(partition) == PARTITIONS["doc_zigzag"] else 0
+    ws = torch.empty(max(256, 4 * (n_docs + 1), need), dtype=torch.uint8, device=device)
     st = load_library().ra_classify(ctypes.byref(shape), cu_ptr, n_docs, int(cp_size), int(rank), _part(partition),
                                     int(bm), int(bn), _ptr(cls), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "ra_classify")

@@ -3,6 +3,8 @@
 // then enqueues its kernels on the caller's stream.
 #include <math.h>
 
+#include <vector>
+
 #include "../../include/ra.h"
 #include "ra_common.h"
 #include "ra_host.h"
@@ -16,23 +18,81 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-ra_status run_plan(const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition, const ra_shape* shape,
-                   void* workspace, hipStream_t st) {
-  const Layout L = attn_layout(shape, cp, nd);
-  char* ws = (char*)workspace;
-  int* dcu = nd > 1 ? (int*)(ws + L.cu_off) : nullptr;
-  if (nd > 1 && launch_upload_i32(cu, nd + 1, dcu, st) != hipSuccess) return RA_ERR_HIP;
-  if (launch_worklist(dcu, nd, (int)shape->s_total, L.s_local, cp, rank, partition, shape->causal, L.bm, L.bn, L.nqt,
-                      L.nkt, L.wl_stride, (int*)(ws + L.wl_off), (int*)(ws + L.count_off), (int*)(ws + L.order_off),
-                      st) != hipSuccess)
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Compact doc-zigzag tables (ra_classify, cp_reorder_docs): cu, block prefix, descriptors.
+struct DocRegions {
+  size_t cu_off, prefix_off, blk_off, total;
+  int nblk;
+};
+
+DocRegions doc_regions(int32_t nd, int32_t cp, int64_t s_local) {
+  DocRegions R{};
+  R.cu_off = 0;
+  R.prefix_off = round256((size_t)(nd + 1) * 4);
+  R.blk_off = R.prefix_off + round256((size_t)(nd + 1) * 4);
+  R.nblk = (int)(s_local / 64);
+  R.total = R.blk_off + (size_t)cp * R.nblk * 8;
+  return R;
+}
+
+ra_status upload_doc_tables(char* ws, const DocRegions& R, const ra_shape* shape, const int32_t* cu, int32_t nd,
+                            int32_t cp, hipStream_t st) {
+  std::vector<int32_t> one{0, (int32_t)shape->s_total}, prefix((size_t)nd + 1);
+  const int32_t* hcu = cu ? cu : one.data();
+  local_len(shape, cp, RA_PART_DOC_ZIGZAG, cu, nd, prefix.data());
+  int* dcu = (int*)(ws + R.cu_off);
+  if (launch_upload_i32(hcu, nd + 1, dcu, st) != hipSuccess ||
+      launch_upload_i32(prefix.data(), nd + 1, (int*)(ws + R.prefix_off), st) != hipSuccess ||
+      launch_doc_blocks(dcu, (const int*)(ws + R.prefix_off), nd, cp, R.nblk, (int2*)(ws + R.blk_off), st) !=
+          hipSuccess)
     return RA_ERR_HIP;
   return RA_OK;
 }
 
-ra_status run_attention(const void* q, const void* k, const void* v, int32_t nd, int32_t cp, int32_t rank,
-                        int32_t partition, const ra_shape* shape, void* out, float* lse, float* o_steps,
+// Layout of the attention workspace for validated arguments (host cu_seqlens, or NULL).
+Layout layout_for(const ra_shape* shape, int32_t cp, int32_t partition, const int32_t* cu, int32_t nd) {
+  return attn_layout(shape, cp, nd, partition, local_len(shape, cp, partition, cu, nd, nullptr));
+}
+
+// Uploads cu_seqlens (and, for doc-zigzag, the block prefix, then builds the block
+// descriptors); the device pointers land in the layout's regions of `workspace`.
+ra_status upload_docs(const Layout& L, const int32_t* cu, int32_t nd, int32_t cp, int32_t partition,
+                      const ra_shape* shape, char* ws, hipStream_t st) {
+  int* dcu = (int*)(ws + L.cu_off);
+  if (L.doczig) {
+    std::vector<int32_t> one{0, (int32_t)shape->s_total}, prefix((size_t)nd + 1);
+    const int32_t* hcu = cu ? cu : one.data();
+    local_len(shape, cp, partition, cu, nd, prefix.data());
+    if (launch_upload_i32(hcu, nd + 1, dcu, st) != hipSuccess ||
+        launch_upload_i32(prefix.data(), nd + 1, (int*)(ws + L.prefix_off), st) != hipSuccess ||
+        launch_doc_blocks(dcu, (const int*)(ws + L.prefix_off), nd, cp, L.nblk, (int2*)(ws + L.blk_off), st) !=
+            hipSuccess)
+      return RA_ERR_HIP;
+  } else if (nd > 1 && launch_upload_i32(cu, nd + 1, dcu, st) != hipSuccess) {
+    return RA_ERR_HIP;
+  }
+  return RA_OK;
+}
+
+ra_status run_plan(const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition, const ra_shape* shape,
+                   void* workspace, hipStream_t st) {
+  const Layout L = layout_for(shape, cp, partition, cu, nd);
+  char* ws = (char*)workspace;
+  const ra_status u = upload_docs(L, cu, nd, cp, partition, shape, ws, st);
+  if (u != RA_OK) return u;
+  const int* dcu = nd > 1 ? (const int*)(ws + L.cu_off) : nullptr;
+  const int2* blk = L.doczig ? (const int2*)(ws + L.blk_off) : nullptr;
+  if (launch_worklist(dcu, blk, nd, (int)shape->s_total, L.s_local, cp, rank, partition, shape->causal, L.bm, L.bn,
+                      L.nqt, L.nkt, L.wl_stride, (int*)(ws + L.wl_off), (int*)(ws + L.count_off),
+                      (int*)(ws + L.order_off), st) != hipSuccess)
+    return RA_ERR_HIP;
+  return RA_OK;
+}
+
+ra_status run_attention(const void* q, const void* k, const void* v, const Layout& L, int32_t nd, int32_t cp,
+                        int32_t rank, int32_t partition, const ra_shape* shape, void* out, float* lse, float* o_steps,
                         float* lse_steps, void* workspace, hipStream_t st, bool steps) {
-  const Layout L = attn_layout(shape, cp, nd);
   char* ws = (char*)workspace;
   const float scale = shape->softmax_scale > 0.f ? shape->softmax_scale : 1.f / sqrtf((float)shape->d);
   AttnArgs a{};
@@ -44,6 +104,7 @@ ra_status run_attention(const void* q, const void* k, const void* v, int32_t nd,
   a.o_steps = o_steps;
   a.lse_steps = lse_steps;
   a.cu = nd > 1 ? (const int*)(ws + L.cu_off) : nullptr;
+  a.blk = L.doczig ? (const int2*)(ws + L.blk_off) : nullptr;
   a.wl = (const int*)(ws + L.wl_off);
   a.wl_count = (const int*)(ws + L.count_off);
   a.order = (const int*)(ws + L.order_off);
@@ -68,13 +129,14 @@ ra_status run_attention(const void* q, const void* k, const void* v, int32_t nd,
 ra_status run_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
                        const void* dout, const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition,
                        const ra_shape* shape, float* dq, float* dk, float* dv, void* workspace, hipStream_t st) {
-  const BwdLayout B = bwd_layout(shape, cp, nd);
+  const BwdLayout B = bwd_layout(shape, cp, nd, partition, local_len(shape, cp, partition, cu, nd, nullptr));
   const Layout& L = B.fwd;
   char* ws = (char*)workspace;
   const ra_status p = run_plan(cu, nd, cp, rank, partition, shape, workspace, st);
   if (p != RA_OK) return p;
   const int* dcu = nd > 1 ? (const int*)(ws + L.cu_off) : nullptr;
-  if (launch_kv_worklist(dcu, nd, (int)shape->s_total, L.s_local, cp, rank, partition, shape->causal, B.bq, B.bk,
+  const int2* blk = L.doczig ? (const int2*)(ws + L.blk_off) : nullptr;
+  if (launch_kv_worklist(dcu, blk, nd, (int)shape->s_total, L.s_local, cp, rank, partition, shape->causal, B.bq, B.bk,
                          B.nqt_kv, B.nkt_kv, B.kwl_stride, (int*)(ws + B.kwl_off), (int*)(ws + B.kcount_off),
                          (int*)(ws + B.korder_off), st) != hipSuccess)
     return RA_ERR_HIP;
@@ -94,6 +156,7 @@ ra_status run_backward(const void* q, const void* k, const void* v, const void* 
   a.dk = dk;
   a.dv = dv;
   a.cu = dcu;
+  a.blk = blk;
   a.wl = (const int*)(ws + L.wl_off);
   a.wl_count = (const int*)(ws + L.count_off);
   a.order = (const int*)(ws + L.order_off);
@@ -144,9 +207,13 @@ const char* ra_status_string(ra_status s) {
 
 size_t ra_workspace_size(const ra_shape* shape, int32_t cp_size, int32_t n_docs) {
   if (!shape || shape->s_total < 1 || shape->s_total > ((int64_t)1 << 30)) return 0;
-  if (cp_size < 1 || cp_size > 64 || shape->s_total % cp_size) return 0;
+  if (cp_size < 1 || cp_size > 64) return 0;
   if (shape->in_dtype != RA_BF16 && shape->in_dtype != RA_F32) return 0;
-  return attn_layout(shape, cp_size, n_docs > 1 ? n_docs : 1).total;
+  // enough for every partition: the doc-zigzag bound on the local length, with its regions
+  const int32_t nd = n_docs > 1 ? n_docs : 1;
+  const size_t plain = attn_layout(shape, cp_size, nd, RA_PART_CONTIGUOUS, shape->s_total / cp_size).total;
+  const size_t docs = attn_layout(shape, cp_size, nd, RA_PART_DOC_ZIGZAG, local_len_bound(shape, cp_size, nd)).total;
+  return plain > docs ? plain : docs;
 }
 
 ra_status ra_forward(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_docs,
@@ -159,7 +226,8 @@ ra_status ra_forward(const void* q, const void* k, const void* v, const int32_t*
   const int32_t nd = effective_docs(cu_seqlens, n_docs);
   const ra_status p = run_plan(cu_seqlens, nd, cp_size, rank, partition, shape, workspace, st);
   if (p != RA_OK) return p;
-  return run_attention(q, k, v, nd, cp_size, rank, partition, shape, out, lse, nullptr, nullptr, workspace, st, false);
+  return run_attention(q, k, v, layout_for(shape, cp_size, partition, cu_seqlens, nd), nd, cp_size, rank, partition,
+                       shape, out, lse, nullptr, nullptr, workspace, st, false);
 }
 
 ra_status ra_plan(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size, int32_t rank,
@@ -177,8 +245,8 @@ ra_status ra_forward_planned(const void* q, const void* k, const void* v, int32_
                                             ws_bytes);
   if (s != RA_OK) return s;
   const int32_t nd = n_docs > 1 ? n_docs : 1;
-  return run_attention(q, k, v, nd, cp_size, rank, partition, shape, out, lse, nullptr, nullptr, workspace,
-                       as_stream(stream), false);
+  return run_attention(q, k, v, attn_layout(shape, cp_size, nd, partition, shape->s_total / cp_size), nd, cp_size,
+                       rank, partition, shape, out, lse, nullptr, nullptr, workspace, as_stream(stream), false);
 }
 
 ra_status ra_forward_steps(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_docs,
@@ -191,16 +259,20 @@ ra_status ra_forward_steps(const void* q, const void* k, const void* v, const in
   const int32_t nd = effective_docs(cu_seqlens, n_docs);
   const ra_status p = run_plan(cu_seqlens, nd, cp_size, rank, partition, shape, workspace, st);
   if (p != RA_OK) return p;
-  return run_attention(q, k, v, nd, cp_size, rank, partition, shape, nullptr, nullptr, o_steps, lse_steps, workspace,
-                       st, true);
+  return run_attention(q, k, v, layout_for(shape, cp_size, partition, cu_seqlens, nd), nd, cp_size, rank, partition,
+                       shape, nullptr, nullptr, o_steps, lse_steps, workspace, st, true);
 }
 
 size_t ra_backward_workspace_size(const ra_shape* shape, int32_t cp_size, int32_t n_docs) {
   if (!shape || shape->s_total < 1 || shape->s_total > ((int64_t)1 << 30)) return 0;
-  if (cp_size < 1 || cp_size > 64 || shape->s_total % cp_size) return 0;
+  if (cp_size < 1 || cp_size > 64) return 0;
   if (shape->in_dtype != RA_BF16 && shape->in_dtype != RA_F32) return 0;
   if (shape->hq < 1 || shape->hq > 4096) return 0;
-  return bwd_layout(shape, cp_size, n_docs > 1 ? n_docs : 1).total;
+  // enough for every partition (the doc-zigzag bound on the local length)
+  const int32_t nd = n_docs > 1 ? n_docs : 1;
+  const size_t plain = bwd_layout(shape, cp_size, nd, RA_PART_CONTIGUOUS, shape->s_total / cp_size).total;
+  const size_t docs = bwd_layout(shape, cp_size, nd, RA_PART_DOC_ZIGZAG, local_len_bound(shape, cp_size, nd)).total;
+  return plain > docs ? plain : docs;
 }
 
 ra_status ra_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -232,12 +304,21 @@ ra_status ra_classify(const ra_shape* shape, const int32_t* cu_seqlens, int32_t 
   if (s != RA_OK) return s;
   const hipStream_t st = as_stream(stream);
   const int32_t nd = effective_docs(cu_seqlens, n_docs);
+  const int s_local = (int)local_len(shape, cp_size, partition, cu_seqlens, nd, nullptr);
   int* dcu = nd > 1 ? (int*)workspace : nullptr;
-  if (nd > 1 && launch_upload_i32(cu_seqlens, nd + 1, dcu, st) != hipSuccess) return RA_ERR_HIP;
-  const int s_local = (int)(shape->s_total / cp_size);
+  const int2* blk = nullptr;
+  if (partition == RA_PART_DOC_ZIGZAG) {
+    const DocRegions R = doc_regions(nd, cp_size, s_local);
+    const ra_status u = upload_doc_tables((char*)workspace, R, shape, cu_seqlens, nd, cp_size, st);
+    if (u != RA_OK) return u;
+    dcu = nd > 1 ? (int*)((char*)workspace + R.cu_off) : nullptr;
+    blk = (const int2*)((char*)workspace + R.blk_off);
+  } else if (nd > 1 && launch_upload_i32(cu_seqlens, nd + 1, dcu, st) != hipSuccess) {
+    return RA_ERR_HIP;
+  }
   const int nqt = (s_local + bm - 1) / bm, nkt = (s_local + bn - 1) / bn;
-  return launch_classify(dcu, nd, (int)shape->s_total, s_local, cp_size, rank, partition, shape->causal, bm, bn, nqt,
-                         nkt, cls, st) == hipSuccess
+  return launch_classify(dcu, blk, nd, (int)shape->s_total, s_local, cp_size, rank, partition, shape->causal, bm, bn,
+                         nqt, nkt, cls, st) == hipSuccess
              ? RA_OK
              : RA_ERR_HIP;
 }
@@ -288,6 +369,7 @@ ra_status usp_forward(const void* q, const void* k, const void* v, const int32_t
   char* ws = (char*)workspace;
   char *QU = ws + U.q_off, *KU = ws + U.k_off, *VU = ws + U.v_off, *OU = ws + U.o_off;
   void* plan = ws + U.plan_off;
+  const Layout plan_layout = attn_layout(&U.slice, ring, nd, partition, sl);
   // 1. Ulysses all-to-all inside every ring group r: device (u, r)'s head slice lands at [u][r]
   for (int32_t r = 0; r < ring; ++r) {
     const int64_t gq = r * ulysses * shard * hq * d * ei, gk = r * ulysses * shard * hkv * d * ei;
@@ -306,7 +388,8 @@ ra_status usp_forward(const void* q, const void* k, const void* v, const int32_t
     for (int32_t u = 0; u < ulysses; ++u) {
       const int64_t dev = (int64_t)u * ring + r;
       const ra_status a = run_attention(QU + dev * sl * hqs * d * ei, KU + (int64_t)u * ring * sl * hkvs * d * ei,
-                                        VU + (int64_t)u * ring * sl * hkvs * d * ei, nd, ring, r, partition, &U.slice,
+                                        VU + (int64_t)u * ring * sl * hkvs * d * ei, plan_layout, nd, ring, r,
+                                        partition, &U.slice,
                                         OU + dev * sl * hqs * d * eo, lse + dev * hqs * sl, nullptr, nullptr, plan, st,
                                         false);
       if (a != RA_OK) return a;
@@ -319,6 +402,48 @@ ra_status usp_forward(const void* q, const void* k, const void* v, const int32_t
       return RA_ERR_HIP;
   }
   return RA_OK;
+}
+
+int64_t ra_local_length(int64_t s_total, int32_t cp_size, int32_t partition, const int32_t* cu_seqlens,
+                        int32_t n_docs) {
+  if (s_total < 1 || s_total > ((int64_t)1 << 30) || cp_size < 1 || cp_size > 64) return -1;
+  if (partition < RA_PART_CONTIGUOUS || partition > RA_PART_DOC_ZIGZAG) return -1;
+  if (check_cu(cu_seqlens, n_docs, s_total) != RA_OK) return -1;
+  ra_shape shp{};
+  shp.s_total = s_total;
+  if (partition != RA_PART_DOC_ZIGZAG) {
+    const int64_t div = partition == RA_PART_ZIGZAG ? 2 * (int64_t)cp_size : cp_size;
+    return s_total % div == 0 ? s_total / cp_size : -1;
+  }
+  return local_len(&shp, cp_size, partition, cu_seqlens, effective_docs(cu_seqlens, n_docs), nullptr);
+}
+
+size_t ra_doc_workspace_size(int64_t s_total, int32_t cp_size, const int32_t* cu_seqlens, int32_t n_docs) {
+  const int64_t sl = ra_local_length(s_total, cp_size, RA_PART_DOC_ZIGZAG, cu_seqlens, n_docs);
+  if (sl < 1) return 0;
+  return doc_regions(effective_docs(cu_seqlens, n_docs), cp_size, sl).total;
+}
+
+ra_status cp_reorder_docs(const void* in, void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
+                          int32_t cp_size, const int32_t* cu_seqlens, int32_t n_docs, int32_t inverse,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  const ra_status c =
+      check_cp_reorder_docs(in, out, s, h, d, elem_bytes, cp_size, cu_seqlens, n_docs, inverse, workspace, ws_bytes);
+  if (c != RA_OK) return c;
+  const hipStream_t st = as_stream(stream);
+  const int32_t nd = effective_docs(cu_seqlens, n_docs);
+  ra_shape shp{};
+  shp.s_total = s;
+  const int64_t sl = local_len(&shp, cp_size, RA_PART_DOC_ZIGZAG, cu_seqlens, nd, nullptr);
+  const DocRegions R = doc_regions(nd, cp_size, sl);
+  char* ws = (char*)workspace;
+  const ra_status u = upload_doc_tables(ws, R, &shp, cu_seqlens, nd, cp_size, st);
+  if (u != RA_OK) return u;
+  return launch_cp_reorder_docs(in, out, s, (int64_t)h * d * elem_bytes, cp_size, (int)sl,
+                                (const int*)(ws + R.cu_off), (const int*)(ws + R.prefix_off),
+                                (const int2*)(ws + R.blk_off), nd, inverse, st) == hipSuccess
+             ? RA_OK
+             : RA_ERR_HIP;
 }
 
 ra_status cp_reorder(const void* in, void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes, int32_t cp_size,

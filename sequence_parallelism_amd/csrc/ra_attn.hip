@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
   if (qt < 0 || qt >= a.nqt) return;  // plan made for other arguments: nothing safe to do
   const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
   const int g = h / (a.hq / a.hkv);
-  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
   const int row = qt * BM + wave * 32 + l32;
   const bool row_ok = row < a.s_local;
   const float C = a.scale_log2;
@@ -346,7 +346,7 @@ __global__ void __launch_bounds__(64) ring_attn_f32_kernel(const AttnArgs a) {
   if (qt < 0 || qt >= a.nqt) return;
   const int h = blockIdx.x % a.hq;
   const int g = h / (a.hq / a.hkv);
-  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
   const int row = qt * BM + lane;
   const bool row_ok = row < a.s_local;
   const float C = a.scale_log2;

@@ -38,6 +38,7 @@ hipError_t launch_upload_i32(const int32_t* host, int n, int32_t* dst, hipStream
 // ---------------------------------------------------------------------------
 struct WlArgs {
   const int* cu;
+  const int2* blk;
   int n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, wl_stride;
   int* wl;
   int* wl_count;
@@ -47,7 +48,7 @@ __global__ void __launch_bounds__(256) worklist_kernel(const WlArgs w) {
   __shared__ int wave_tot[4];
   const int I = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const PartInfo p{w.part, w.s_local, w.cp};
+  const PartInfo p{w.part, w.s_local, w.cp, w.blk};
   const int qa = I * w.bm;
   const int qb = qa + w.bm < w.s_local ? qa + w.bm : w.s_local;
   const int nent = w.cp * w.nkt;
@@ -100,11 +101,11 @@ __global__ void __launch_bounds__(1024) order_kernel(const int* count, int nqt, 
   }
 }
 
-hipError_t launch_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
-                           int causal, int bm, int bn, int nqt, int nkt, int wl_stride, int* wl, int* wl_count,
-                           int* order, hipStream_t st) {
+hipError_t launch_worklist(const int* cu, const int2* blk, int n_docs, int s_total, int s_local, int cp, int rank,
+                           int part, int causal, int bm, int bn, int nqt, int nkt, int wl_stride, int* wl,
+                           int* wl_count, int* order, hipStream_t st) {
   if (nqt == 0) return hipSuccess;
-  WlArgs w{cu, n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, wl_stride, wl, wl_count};
+  WlArgs w{cu, blk, n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, wl_stride, wl, wl_count};
   hipLaunchKernelGGL(worklist_kernel, dim3(nqt), dim3(256), 0, st, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -118,10 +119,150 @@ hipError_t launch_order(const int* count, int n, int* order, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// Doc-zigzag block descriptors. Rank r's local slots are, document after
+// document, piece r then piece 2cp-1-r of that document, each piece padded to
+// half = (prefix[j+1] - prefix[j]) / 2 blocks. Pieces hold floor(L/2cp) or one
+// more tokens (the first L mod 2cp pieces the extra one), real tokens first.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) doc_blocks_kernel(const int* cu, const int* prefix, int n_docs, int cp,
+                                                         int nblk, int2* blk) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= cp * nblk) return;
+  const int r = idx / nblk, b = idx - r * nblk;
+  int lo = 0, hi = n_docs - 1;  // document: largest j with prefix[j] <= b
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  const int j = lo;
+  const int half = (prefix[j + 1] - prefix[j]) >> 1;
+  const int lb = b - prefix[j];
+  const int piece = lb < half ? r : 2 * cp - 1 - r;
+  const int bip = lb < half ? lb : lb - half;
+  const int L = cu[j + 1] - cu[j], n = 2 * cp;
+  const int q = L / n, rem = L % n;
+  const int pstart = piece * q + (piece < rem ? piece : rem);
+  const int psize = q + (piece < rem ? 1 : 0);
+  int cnt = psize - bip * kDocBlock;
+  cnt = cnt < 0 ? 0 : (cnt > kDocBlock ? kDocBlock : cnt);
+  blk[idx] = make_int2(cu[j] + pstart + bip * kDocBlock, cnt);
+}
+
+hipError_t launch_doc_blocks(const int* cu, const int* prefix, int n_docs, int cp, int nblk, int2* blk,
+                             hipStream_t st) {
+  const long long n = (long long)cp * nblk;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(doc_blocks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cu, prefix, n_docs, cp,
+                     nblk, blk);
+  return hipGetLastError();
+}
+
+// Doc-zigzag reorder, one wave per destination row. Forward: row R = (rank, slot)
+// takes global row pos(rank, slot), or zeros for padding. Inverse: global row p
+// takes the slot that holds it (document j by binary search in cu, piece and
+// offset from the piece sizes).
+struct DocCopyArgs {
+  const void* in;
+  void* out;
+  long long nrows;   // destination rows
+  long long cpr;     // chunks per row
+  int s_local, cp, n_docs;
+  const int* cu;
+  const int* prefix;
+  const int2* blk;
+};
+
+__device__ __forceinline__ long long doc_src_row(const DocCopyArgs& c, long long R, bool inverse) {
+  if (!inverse) {
+    const int r = (int)(R / c.s_local), i = (int)(R - (long long)r * c.s_local);
+    const int2 b = c.blk[r * (c.s_local / kDocBlock) + i / kDocBlock];
+    const int o = i % kDocBlock;
+    return o < b.y ? (long long)(b.x + o) : -1;
+  }
+  const int p = (int)R;
+  int lo = 0, hi = c.n_docs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (c.cu[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  const int j = lo, rel = p - c.cu[j];
+  const int L = c.cu[j + 1] - c.cu[j], n = 2 * c.cp, q = L / n, rem = L % n;
+  int k, off;
+  if (rel < rem * (q + 1)) {
+    k = rel / (q + 1);
+    off = rel - k * (q + 1);
+  } else {
+    k = rem + (rel - rem * (q + 1)) / q;
+    off = rel - rem * (q + 1) - (k - rem) * q;
+  }
+  const int half = (c.prefix[j + 1] - c.prefix[j]) >> 1;
+  const int r = k < c.cp ? k : n - 1 - k;
+  const int i = c.prefix[j] * kDocBlock + (k < c.cp ? 0 : half * kDocBlock) + off;
+  return (long long)r * c.s_local + i;
+}
+
+template <typename T, bool INVERSE>
+__global__ void __launch_bounds__(256) copy_doc_rows_kernel(const DocCopyArgs c) {
+  const int lane = threadIdx.x & 63;
+  const long long nw = (long long)gridDim.x * 4;
+  for (long long R = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); R < c.nrows; R += nw) {
+    const long long S = doc_src_row(c, R, INVERSE);
+    T* dst = (T*)c.out + R * c.cpr;
+    if (S < 0) {
+      for (long long i = lane; i < c.cpr; i += 64) dst[i] = T{};
+      continue;
+    }
+    const T* src = (const T*)c.in + S * c.cpr;
+    long long i = lane;
+    for (; i + 192 < c.cpr; i += 256) {
+      const T a0 = src[i], a1 = src[i + 64], a2 = src[i + 128], a3 = src[i + 192];
+      dst[i] = a0;
+      dst[i + 64] = a1;
+      dst[i + 128] = a2;
+      dst[i + 192] = a3;
+    }
+    for (; i < c.cpr; i += 64) dst[i] = src[i];
+  }
+}
+
+template <bool INVERSE>
+static hipError_t launch_doc_copy(DocCopyArgs c, long long row_bytes, hipStream_t st) {
+  if (c.nrows == 0 || row_bytes == 0) return hipSuccess;
+  long long blocks = (c.nrows + 3) / 4;
+  if (blocks > 65536) blocks = 65536;
+  const uintptr_t al = (uintptr_t)c.in | (uintptr_t)c.out | (uintptr_t)row_bytes;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (al % 16 == 0) {
+    c.cpr = row_bytes / 16;
+    hipLaunchKernelGGL((copy_doc_rows_kernel<uint4, INVERSE>), grid, block, 0, st, c);
+  } else if (al % 4 == 0) {
+    c.cpr = row_bytes / 4;
+    hipLaunchKernelGGL((copy_doc_rows_kernel<uint32_t, INVERSE>), grid, block, 0, st, c);
+  } else {
+    c.cpr = row_bytes;
+    hipLaunchKernelGGL((copy_doc_rows_kernel<uint8_t, INVERSE>), grid, block, 0, st, c);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cp_reorder_docs(const void* in, void* out, int64_t s, int64_t row_bytes, int cp, int s_local,
+                                  const int* cu, const int* prefix, const int2* blk, int n_docs, int inverse,
+                                  hipStream_t st) {
+  DocCopyArgs c{in, out, 0, 0, s_local, cp, n_docs, cu, prefix, blk};
+  if (inverse) {
+    c.nrows = s;
+    return launch_doc_copy<true>(c, row_bytes, st);
+  }
+  c.nrows = (long long)cp * s_local;
+  return launch_doc_copy<false>(c, row_bytes, st);
+}
+
+// ---------------------------------------------------------------------------
 // Public tile classification: one thread per (step, query tile, key tile).
 // ---------------------------------------------------------------------------
 struct ClsArgs {
   const int* cu;
+  const int2* blk;
   int n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt;
   int8_t* cls;
 };
@@ -133,18 +274,18 @@ __global__ void __launch_bounds__(256) classify_kernel(const ClsArgs c) {
   const int t = (int)(idx / per_step);
   const long long rem = idx - t * per_step;
   const int I = (int)(rem / c.nkt), J = (int)(rem - (long long)I * c.nkt);
-  const PartInfo p{c.part, c.s_local, c.cp};
+  const PartInfo p{c.part, c.s_local, c.cp, c.blk};
   const int owner = (c.rank - t + c.cp) % c.cp;
   const int qa = I * c.bm, qb = qa + c.bm < c.s_local ? qa + c.bm : c.s_local;
   const int ka = J * c.bn, kb = ka + c.bn < c.s_local ? ka + c.bn : c.s_local;
   c.cls[idx] = (int8_t)classify_tile(p, c.rank, qa, qb, owner, ka, kb, c.cu, c.n_docs, c.s_total, c.causal);
 }
 
-hipError_t launch_classify(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
-                           int causal, int bm, int bn, int nqt, int nkt, int8_t* cls, hipStream_t st) {
+hipError_t launch_classify(const int* cu, const int2* blk, int n_docs, int s_total, int s_local, int cp, int rank,
+                           int part, int causal, int bm, int bn, int nqt, int nkt, int8_t* cls, hipStream_t st) {
   const long long total = (long long)cp * nqt * nkt;
   if (total == 0) return hipSuccess;
-  ClsArgs c{cu, n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, cls};
+  ClsArgs c{cu, blk, n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, cls};
   hipLaunchKernelGGL(classify_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, c);
   return hipGetLastError();
 }
@@ -249,7 +390,7 @@ template <int KIND>
 __device__ __forceinline__ long long src_row(const CopyArgs& c, long long R) {
   if constexpr (KIND == MAP_REORDER_FWD) {
     const int r = (int)(R / c.s_local), i = (int)(R - (long long)r * c.s_local);
-    return pos_of(PartInfo{c.part, c.s_local, c.cp}, r, i);
+    return pos_of(PartInfo{c.part, c.s_local, c.cp, nullptr}, r, i);
   } else if constexpr (KIND == MAP_REORDER_INV) {
     const int p = (int)R;
     int r, i;

@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
   if (qt < 0 || qt >= a.nqt) return;
   const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
   const int g = h / (a.hq / a.hkv);
-  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
   const int row = qt * BM + wave * 32 + l32;
   const bool row_ok = row < a.s_local;
   const float C = a.scale_log2;
@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
   const int g = head_of_slot(blockIdx.x % a.hkv, a.hkv);
   const int G = a.hq / a.hkv;
   const int owner = kt / a.nkt_kv, J = kt - owner * a.nkt_kv;
-  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
   const int key = J * BK + wave * 32 + l32;
   const bool key_ok = key < a.s_local;
   const float C = a.scale_log2;
@@ -591,7 +591,7 @@ __global__ void __launch_bounds__(64) ring_bwd_dq_f32_kernel(const BwdArgs a) {
   if (qt < 0 || qt >= a.nqt) return;
   const int h = blockIdx.x % a.hq;
   const int g = h / (a.hq / a.hkv);
-  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
   const int row = qt * BM + lane;
   const bool row_ok = row < a.s_local;
   const float C = a.scale_log2;
@@ -683,7 +683,7 @@ __global__ void __launch_bounds__(64) ring_bwd_dkv_f32_kernel(const BwdArgs a) {
   const int g = blockIdx.x % a.hkv;
   const int G = a.hq / a.hkv;
   const int owner = kt / a.nkt_kv, J = kt - owner * a.nkt_kv;
-  const PartInfo pinfo{a.part, a.s_local, a.cp};
+  const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
   const int key = J * BK + lane;
   const bool key_ok = key < a.s_local;
   const float C = a.scale_log2;
@@ -770,6 +770,7 @@ __global__ void __launch_bounds__(64) ring_bwd_dkv_f32_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------
 struct KvWlArgs {
   const int* cu;
+  const int2* blk;
   int n_docs, s_total, s_local, cp, rank, part, causal, bq, bk, nqt, nkt, stride;
   int* wl;
   int* count;
@@ -779,7 +780,7 @@ __global__ void __launch_bounds__(256) kv_worklist_kernel(const KvWlArgs w) {
   __shared__ int wave_tot[4];
   const int kt = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const PartInfo p{w.part, w.s_local, w.cp};
+  const PartInfo p{w.part, w.s_local, w.cp, w.blk};
   const int owner = kt / w.nkt, J = kt - owner * w.nkt;
   const int ka = J * w.bk;
   const int kb = ka + w.bk < w.s_local ? ka + w.bk : w.s_local;
@@ -810,12 +811,12 @@ __global__ void __launch_bounds__(256) kv_worklist_kernel(const KvWlArgs w) {
   if (tid == 0) w.count[kt] = base;
 }
 
-hipError_t launch_kv_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
-                              int causal, int bq, int bk, int nqt, int nkt, int stride, int* wl, int* count,
+hipError_t launch_kv_worklist(const int* cu, const int2* blk, int n_docs, int s_total, int s_local, int cp, int rank,
+                              int part, int causal, int bq, int bk, int nqt, int nkt, int stride, int* wl, int* count,
                               int* order, hipStream_t st) {
   const int n = cp * nkt;
   if (n == 0) return hipSuccess;
-  KvWlArgs w{cu, n_docs, s_total, s_local, cp, rank, part, causal, bq, bk, nqt, nkt, stride, wl, count};
+  KvWlArgs w{cu, blk, n_docs, s_total, s_local, cp, rank, part, causal, bq, bk, nqt, nkt, stride, wl, count};
   hipLaunchKernelGGL(kv_worklist_kernel, dim3(n), dim3(256), 0, st, w);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -6,6 +6,12 @@
 //   striped:    pos = owner + cp*i                     (one run, stride cp)
 //   zigzag:     i <  S_l/2: pos = owner*half + i       (run 1, stride 1)
 //               i >= S_l/2: pos = (2cp-1-owner)*half + (i - half)   (run 2)
+//   doc-zigzag: every packed document is cut into 2cp pieces padded to
+//               multiples of 64 slots; local index i lies in 64-slot block
+//               i / 64, whose first `cnt` slots hold positions start, start+1,
+//               ... (a per-block descriptor) and whose other slots are padding
+//               (position -1). An aligned range of at most 128 indices spans at
+//               most two blocks, so it is at most two runs as well.
 // (partition definitions: ra.h, RA_PART_*; zigzag and striped are the
 // load-balancing reorders named on the long-context deep-dive page's timeline.)
 //
@@ -20,7 +26,10 @@
 
 namespace ra {
 
-enum { PART_CONTIGUOUS = 0, PART_ZIGZAG = 1, PART_STRIPED = 2 };
+enum { PART_CONTIGUOUS = 0, PART_ZIGZAG = 1, PART_STRIPED = 2, PART_DOC_ZIGZAG = 3 };
+
+// Slots per doc-zigzag block (pieces are padded to a multiple of this).
+constexpr int kDocBlock = 64;
 enum { CLS_SKIP = 0, CLS_PARTIAL = 1, CLS_FULL = 2 };
 
 // Work-list entry: bits 0-1 class, bits 2-7 ring step, bits 8-31 key tile.
@@ -40,10 +49,16 @@ struct PartInfo {
   int part;  // PART_*
   int s_local;
   int cp;
+  const int2* blk;  // doc-zigzag: [cp][s_local / 64] block descriptors {start, cnt}
 };
 
-// Global position of local index i of `owner`.
+// Global position of local index i of `owner` (-1: doc-zigzag padding).
 __device__ __forceinline__ int pos_of(const PartInfo& p, int owner, int i) {
+  if (p.part == PART_DOC_ZIGZAG) {
+    const int2 b = p.blk[owner * (p.s_local / kDocBlock) + i / kDocBlock];
+    const int o = i % kDocBlock;
+    return o < b.y ? b.x + o : -1;
+  }
   if (p.part == PART_CONTIGUOUS) return owner * p.s_local + i;
   if (p.part == PART_STRIPED) return owner + p.cp * i;
   const int half = p.s_local >> 1;
@@ -58,6 +73,20 @@ __device__ __forceinline__ void runs_of(const PartInfo& p, int owner, int a, int
   r0 = Run{0, 1, 0, 0};
   r1 = Run{0, 1, 0, 0};
   if (b <= a) return;
+  if (p.part == PART_DOC_ZIGZAG) {  // [a, b) spans at most two blocks (aligned tiles of <= 128)
+    const int nb = p.s_local / kDocBlock;
+    const int A = a / kDocBlock, oa = a % kDocBlock, ea = (A + 1) * kDocBlock;
+    const int2 ba = p.blk[owner * nb + A];
+    const int e0 = (b < ea ? b : ea) - A * kDocBlock;
+    const int c0 = (e0 < ba.y ? e0 : ba.y) - oa;
+    r0 = Run{ba.x + oa, 1, c0 > 0 ? c0 : 0, 0};
+    if (b > ea) {
+      const int2 bb = p.blk[owner * nb + A + 1];
+      const int c1 = b - ea < bb.y ? b - ea : bb.y;
+      r1 = Run{bb.x, 1, c1 > 0 ? c1 : 0, ea - a};
+    }
+    return;
+  }
   if (p.part == PART_CONTIGUOUS) {
     r0 = Run{owner * p.s_local + a, 1, b - a, 0};
     return;
@@ -87,9 +116,14 @@ __device__ __forceinline__ int doc_of(const int* cu, int n_docs, int p) {
   return lo;
 }
 
-// Visible key-position interval [lo, hi] of query position pq.
+// Visible key-position interval [lo, hi] of query position pq (empty for padding, pq < 0).
 __device__ __forceinline__ void row_interval(const int* cu, int n_docs, int s_total, int causal, int pq,
                                              int& lo, int& hi) {
+  if (pq < 0) {
+    lo = 1;
+    hi = 0;
+    return;
+  }
   if (n_docs <= 1) {
     lo = 0;
     hi = causal ? pq : s_total - 1;
@@ -105,6 +139,11 @@ __device__ __forceinline__ void row_interval(const int* cu, int n_docs, int s_to
 // The same relation as row_interval, solved for the query.
 __device__ __forceinline__ void key_interval(const int* cu, int n_docs, int s_total, int causal, int pk,
                                              int& lo, int& hi) {
+  if (pk < 0) {
+    lo = 1;
+    hi = 0;
+    return;
+  }
   if (n_docs <= 1) {
     lo = causal ? pk : 0;
     hi = s_total - 1;
@@ -185,7 +224,9 @@ __device__ inline int classify_tile(const PartInfo& p, int rank, int qa, int qb,
   pair(q1, k0);
   pair(q1, k1);
   if (!any) return CLS_SKIP;
-  return all ? CLS_FULL : CLS_PARTIAL;
+  // a tile whose runs miss some of its indices (doc-zigzag padding) is never FULL
+  const bool covered = q0.cnt + q1.cnt == qb - qa && k0.cnt + k1.cnt == kb - ka;
+  return all && covered ? CLS_FULL : CLS_PARTIAL;
 }
 
 // Arguments of the attention kernels (one rank, all ring steps).
@@ -198,6 +239,7 @@ struct AttnArgs {
   float* o_steps;     // [cp][S_l][hq][d] (steps mode)
   float* lse_steps;   // [cp][hq][S_l]    (steps mode)
   const int* cu;      // device cu_seqlens [n_docs+1] (unused when n_docs <= 1)
+  const int2* blk;    // doc-zigzag block descriptors (else unused)
   const int* wl;      // work list [nqt][wl_stride]
   const int* wl_count;  // [nqt]
   const int* order;   // [nqt] query tiles, heaviest first
@@ -228,6 +270,7 @@ struct BwdArgs {
   float* dk;           // [cp][S_l][hkv][d]
   float* dv;           // [cp][S_l][hkv][d]
   const int* cu;       // device cu_seqlens [n_docs+1] (unused when n_docs <= 1)
+  const int2* blk;     // doc-zigzag block descriptors (else unused)
   const int* wl;       // dQ kernel: the forward's work list [nqt][wl_stride]
   const int* wl_count;
   const int* order;

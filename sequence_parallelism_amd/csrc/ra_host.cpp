@@ -20,11 +20,22 @@ constexpr int kBwdF32BK = 64, kBwdF32BQ = 32;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool valid_partition(int32_t p) { return p == RA_PART_CONTIGUOUS || p == RA_PART_ZIGZAG || p == RA_PART_STRIPED; }
+bool valid_partition(int32_t p) {
+  return p == RA_PART_CONTIGUOUS || p == RA_PART_ZIGZAG || p == RA_PART_STRIPED || p == RA_PART_DOC_ZIGZAG;
+}
 
 ra_status check_divisible(int64_t s, int32_t cp, int32_t partition) {
+  if (partition == RA_PART_DOC_ZIGZAG) return RA_OK;  // pieces are padded
   if (partition == RA_PART_ZIGZAG) return s % (2 * (int64_t)cp) == 0 ? RA_OK : RA_ERR_DIVISIBILITY;
   return s % cp == 0 ? RA_OK : RA_ERR_DIVISIBILITY;
+}
+
+constexpr int64_t kDocBlock = 64;  // doc-zigzag block (must match the device code)
+
+// Blocks per rank of one document of length L under doc-zigzag.
+int64_t doc_blocks(int64_t L, int32_t cp) {
+  const int64_t longest = (L + 2 * cp - 1) / (2 * cp);
+  return 2 * ((longest + kDocBlock - 1) / kDocBlock);
 }
 
 bool overlaps(const void* a, const void* b, uint64_t bytes) {
@@ -68,9 +79,31 @@ ra_status check_cu(const int32_t* cu, int32_t n_docs, int64_t s_total) {
 
 int32_t effective_docs(const int32_t* cu, int32_t n_docs) { return cu ? n_docs : 1; }
 
-Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev) {
+int64_t local_len(const ra_shape* shape, int32_t cp_size, int32_t partition, const int32_t* cu, int32_t n_docs,
+                  int32_t* prefix) {
+  if (partition != RA_PART_DOC_ZIGZAG) return shape->s_total / cp_size;
+  const int32_t nd = cu ? n_docs : 1;
+  int64_t blocks = 0;
+  if (prefix) prefix[0] = 0;
+  for (int32_t j = 0; j < nd; ++j) {
+    const int64_t L = cu ? (int64_t)cu[j + 1] - cu[j] : shape->s_total;
+    blocks += doc_blocks(L, cp_size);
+    if (blocks * kDocBlock > ((int64_t)1 << 31) - 1) return -1;
+    if (prefix) prefix[j + 1] = (int32_t)blocks;
+  }
+  return blocks * kDocBlock;
+}
+
+int64_t local_len_bound(const ra_shape* shape, int32_t cp_size, int32_t n_docs) {
+  // each document adds at most 2 * 64 slots of rounding over its share L / cp
+  const int64_t nd = n_docs > 1 ? n_docs : 1;
+  const int64_t base = (shape->s_total + cp_size - 1) / cp_size;
+  return ((base + 2 * kDocBlock * nd + 2 + kDocBlock - 1) / kDocBlock) * kDocBlock;
+}
+
+Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition, int64_t s_local) {
   Layout L{};
-  L.s_local = (int)(shape->s_total / cp_size);
+  L.s_local = (int)s_local;
   const bool bf16 = shape->in_dtype == RA_BF16;
   L.bm = bf16 ? kBf16BM : kF32BM;
   L.bn = bf16 ? kBf16BN : kF32BN;
@@ -78,32 +111,48 @@ Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev) {
   L.nkt = (L.s_local + L.bn - 1) / L.bn;
   L.wl_stride = cp_size * L.nkt;
   L.n_docs_dev = n_docs_dev < 1 ? 1 : n_docs_dev;
-  const size_t cu_bytes = L.n_docs_dev > 1 ? (size_t)(L.n_docs_dev + 1) * 4 : 0;
+  L.doczig = partition == RA_PART_DOC_ZIGZAG;
+  L.nblk = L.doczig ? (int)(s_local / kDocBlock) : 0;
+  const size_t cu_bytes = (L.n_docs_dev > 1 || L.doczig) ? (size_t)(L.n_docs_dev + 1) * 4 : 0;
   L.cu_off = 0;
-  L.count_off = align256(L.cu_off + cu_bytes);
+  L.prefix_off = align256(L.cu_off + cu_bytes);
+  L.blk_off = align256(L.prefix_off + (L.doczig ? (size_t)(L.n_docs_dev + 1) * 4 : 0));
+  L.count_off = align256(L.blk_off + (L.doczig ? (size_t)cp_size * L.nblk * 8 : 0));
   L.order_off = align256(L.count_off + (size_t)L.nqt * 4);
   L.wl_off = align256(L.order_off + (size_t)L.nqt * 4);
   L.total = align256(L.wl_off + (size_t)L.nqt * L.wl_stride * 4);
   return L;
 }
 
-BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev) {
+BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition,
+                     int64_t s_local) {
   BwdLayout B{};
-  B.fwd = attn_layout(shape, cp_size, n_docs_dev);
+  B.fwd = attn_layout(shape, cp_size, n_docs_dev, partition, s_local);
   const bool bf16 = shape->in_dtype == RA_BF16;
   B.bk = bf16 ? kBwdBf16BK : kBwdF32BK;
   B.bq = bf16 ? kBwdBf16BQ : kBwdF32BQ;
-  const int s_local = B.fwd.s_local;
-  B.nkt_kv = (s_local + B.bk - 1) / B.bk;
-  B.nqt_kv = (s_local + B.bq - 1) / B.bq;
+  const int sl = B.fwd.s_local;
+  B.nkt_kv = (sl + B.bk - 1) / B.bk;
+  B.nqt_kv = (sl + B.bq - 1) / B.bq;
   B.kwl_stride = B.nqt_kv;
   const size_t n_kt = (size_t)cp_size * B.nkt_kv;
   B.kcount_off = B.fwd.total;
   B.korder_off = align256(B.kcount_off + n_kt * 4);
   B.kwl_off = align256(B.korder_off + n_kt * 4);
   B.dsum_off = align256(B.kwl_off + n_kt * B.kwl_stride * 4);
-  B.total = align256(B.dsum_off + (size_t)shape->hq * s_local * 4);
+  B.total = align256(B.dsum_off + (size_t)shape->hq * sl * 4);
   return B;
+}
+
+// Local length for the arguments, and the 32-bit byte bound of one rank's rows
+// and one chunk at `elem` bytes per element (doc-zigzag lengths exceed S / cp).
+ra_status checked_local_len(const ra_shape* shape, int32_t cp_size, int32_t partition, const int32_t* cu,
+                            int32_t n_docs, int64_t elem, int64_t& s_local) {
+  s_local = local_len(shape, cp_size, partition, cu, n_docs, nullptr);
+  if (s_local < 1) return RA_ERR_SHAPE;
+  const int64_t heads = shape->hq > shape->hkv ? shape->hq : shape->hkv;
+  if (s_local * heads * shape->d * elem > 0x7fffffffLL) return RA_ERR_SHAPE;
+  return RA_OK;
 }
 
 ra_status check_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -116,9 +165,10 @@ ra_status check_backward(const void* q, const void* k, const void* v, const void
   s = check_cu(cu, n_docs, shape->s_total);
   if (s != RA_OK) return s;
   // the fp32 gradients of one rank's rows and of one chunk stay within 2^31 bytes
-  const int64_t heads = shape->hq > shape->hkv ? shape->hq : shape->hkv;
-  if ((shape->s_total / cp_size) * heads * shape->d * 4 > 0x7fffffffLL) return RA_ERR_SHAPE;
-  const BwdLayout B = bwd_layout(shape, cp_size, effective_docs(cu, n_docs));
+  int64_t sl;
+  s = checked_local_len(shape, cp_size, partition, cu, n_docs, 4, sl);
+  if (s != RA_OK) return s;
+  const BwdLayout B = bwd_layout(shape, cp_size, effective_docs(cu, n_docs), partition, sl);
   if ((int64_t)B.fwd.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
   if ((int64_t)cp_size * B.nkt_kv * shape->hkv > 0x7fffffffLL) return RA_ERR_SHAPE;
   if (!workspace || ws_bytes < B.total) return RA_ERR_WORKSPACE;
@@ -133,7 +183,10 @@ ra_status check_forward(const void* q, const void* k, const void* v, const int32
   if (s != RA_OK) return s;
   s = check_cu(cu, n_docs, shape->s_total);
   if (s != RA_OK) return s;
-  const Layout L = attn_layout(shape, cp_size, effective_docs(cu, n_docs));
+  int64_t sl;
+  s = checked_local_len(shape, cp_size, partition, cu, n_docs, shape->in_dtype == RA_BF16 ? 2 : 4, sl);
+  if (s != RA_OK) return s;
+  const Layout L = attn_layout(shape, cp_size, effective_docs(cu, n_docs), partition, sl);
   if ((int64_t)L.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
   if (!workspace || ws_bytes < L.total) return RA_ERR_WORKSPACE;
   return RA_OK;
@@ -146,7 +199,9 @@ ra_status check_plan(const ra_shape* shape, const int32_t* cu, int32_t n_docs, i
   if (s != RA_OK) return s;
   s = check_cu(cu, n_docs, shape->s_total);
   if (s != RA_OK) return s;
-  const Layout L = attn_layout(shape, cp_size, effective_docs(cu, n_docs));
+  // a plan serves ra_forward_planned, which takes no cu_seqlens to size a doc-zigzag share
+  if (partition == RA_PART_DOC_ZIGZAG) return RA_ERR_UNSUPPORTED;
+  const Layout L = attn_layout(shape, cp_size, effective_docs(cu, n_docs), partition, shape->s_total / cp_size);
   if ((int64_t)L.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
   if (!workspace || ws_bytes < L.total) return RA_ERR_WORKSPACE;
   return RA_OK;
@@ -159,10 +214,17 @@ ra_status check_forward_planned(const void* q, const void* k, const void* v, int
   ra_status s = check_shape(shape, cp_size, rank, partition);
   if (s != RA_OK) return s;
   if (n_docs < 0 || n_docs > shape->s_total) return RA_ERR_CU_SEQLENS;
-  const Layout L = attn_layout(shape, cp_size, n_docs > 1 ? n_docs : 1);
+  if (partition == RA_PART_DOC_ZIGZAG) return RA_ERR_UNSUPPORTED;  // its local length needs cu_seqlens
+  const Layout L = attn_layout(shape, cp_size, n_docs > 1 ? n_docs : 1, partition, shape->s_total / cp_size);
   if ((int64_t)L.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
   if (!workspace || ws_bytes < L.total) return RA_ERR_WORKSPACE;
   return RA_OK;
+}
+
+// Compact doc-zigzag tables of ra_classify / cp_reorder_docs: cu and block prefix
+// (256-byte aligned), then the block descriptors.
+size_t classify_doc_ws(int32_t nd, int32_t cp_size, int64_t s_local) {
+  return align256((size_t)(nd + 1) * 4) * 2 + (size_t)cp_size * (size_t)(s_local / kDocBlock) * 8;
 }
 
 ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
@@ -180,7 +242,15 @@ ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_doc
   s = check_cu(cu, n_docs, shape->s_total);
   if (s != RA_OK) return s;
   const int32_t nd = effective_docs(cu, n_docs);
-  const size_t need = nd > 1 ? (size_t)(nd + 1) * 4 : 0;
+  size_t need = nd > 1 ? (size_t)(nd + 1) * 4 : 0;
+  if (partition == RA_PART_DOC_ZIGZAG) {
+    // tiles must not span more than two 64-slot blocks
+    const auto pow2_le128 = [](int32_t x) { return x == 16 || x == 32 || x == 64 || x == 128; };
+    if (!pow2_le128(bm) || !pow2_le128(bn)) return RA_ERR_UNSUPPORTED;
+    const int64_t sl = local_len(shape, cp_size, partition, cu, n_docs, nullptr);
+    if (sl < 1) return RA_ERR_SHAPE;
+    need = classify_doc_ws(nd, cp_size, sl);
+  }
   if (need > 0 && (!workspace || ws_bytes < need)) return RA_ERR_WORKSPACE;
   return RA_OK;
 }
@@ -242,7 +312,7 @@ UspLayout usp_layout(const ra_shape* shape, int32_t ulysses, int32_t ring, int32
   U.v_off = align256(U.k_off + S * shape->hkv * d * ei);
   U.o_off = align256(U.v_off + S * shape->hkv * d * ei);
   U.plan_off = align256(U.o_off + S * shape->hq * d * eo);
-  U.plan_bytes = attn_layout(&U.slice, ring, n_docs_dev).total;
+  U.plan_bytes = attn_layout(&U.slice, ring, n_docs_dev, RA_PART_CONTIGUOUS, shape->s_total / ring).total;
   U.total = align256(U.plan_off + U.plan_bytes);
   return U;
 }
@@ -252,6 +322,7 @@ ra_status check_usp(const void* q, const void* k, const void* v, const int32_t* 
                     const void* workspace, size_t ws_bytes) {
   if (!q || !k || !v || !shape || !out || !lse) return RA_ERR_NULL;
   if (ulysses < 1 || ulysses > kMaxHeads) return RA_ERR_SHAPE;
+  if (partition == RA_PART_DOC_ZIGZAG) return RA_ERR_UNSUPPORTED;
   ra_status s = check_shape(shape, ring, 0, partition);
   if (s != RA_OK) return s;
   if (shape->hq % ulysses != 0 || shape->hkv % ulysses != 0) return RA_ERR_HEADS;
@@ -259,7 +330,7 @@ ra_status check_usp(const void* q, const void* k, const void* v, const int32_t* 
   s = check_cu(cu, n_docs, shape->s_total);
   if (s != RA_OK) return s;
   const UspLayout U = usp_layout(shape, ulysses, ring, effective_docs(cu, n_docs));
-  const Layout L = attn_layout(&U.slice, ring, effective_docs(cu, n_docs));
+  const Layout L = attn_layout(&U.slice, ring, effective_docs(cu, n_docs), partition, shape->s_total / ring);
   if ((int64_t)L.nqt * U.slice.hq > 0x7fffffffLL) return RA_ERR_SHAPE;
   if (!workspace || ws_bytes < U.total) return RA_ERR_WORKSPACE;
   return RA_OK;
@@ -272,12 +343,36 @@ ra_status check_cp_reorder(const void* in, const void* out, int64_t s, int32_t h
   if (cp_size < 1 || cp_size > 65536) return RA_ERR_SHAPE;
   if (inverse != 0 && inverse != 1) return RA_ERR_SHAPE;
   if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return RA_ERR_UNSUPPORTED;
-  if (!valid_partition(partition)) return RA_ERR_UNSUPPORTED;
+  if (!valid_partition(partition) || partition == RA_PART_DOC_ZIGZAG) return RA_ERR_UNSUPPORTED;
   const ra_status st = check_divisible(s, cp_size, partition);
   if (st != RA_OK) return st;
   const uint64_t bytes = (uint64_t)s * (uint64_t)h * (uint64_t)d * (uint64_t)elem_bytes;
   if (bytes > ((uint64_t)1 << 42)) return RA_ERR_SHAPE;
   if (overlaps(in, out, bytes)) return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+ra_status check_cp_reorder_docs(const void* in, const void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
+                                int32_t cp_size, const int32_t* cu, int32_t n_docs, int32_t inverse,
+                                const void* workspace, size_t ws_bytes) {
+  if (!in || !out) return RA_ERR_NULL;
+  if (s < 1 || s > kMaxTokens || h < 1 || d < 1) return RA_ERR_SHAPE;
+  if (cp_size < 1 || cp_size > kMaxCp) return RA_ERR_SHAPE;
+  if (inverse != 0 && inverse != 1) return RA_ERR_SHAPE;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return RA_ERR_UNSUPPORTED;
+  ra_status st = check_cu(cu, n_docs, s);
+  if (st != RA_OK) return st;
+  ra_shape shp{};
+  shp.s_total = s;
+  const int64_t sl = local_len(&shp, cp_size, RA_PART_DOC_ZIGZAG, cu, n_docs, nullptr);
+  if (sl < 1) return RA_ERR_SHAPE;
+  const uint64_t row = (uint64_t)h * (uint64_t)d * (uint64_t)elem_bytes;
+  const uint64_t in_bytes = inverse ? (uint64_t)cp_size * sl * row : (uint64_t)s * row;
+  const uint64_t out_bytes = inverse ? (uint64_t)s * row : (uint64_t)cp_size * sl * row;
+  if (in_bytes > ((uint64_t)1 << 42) || out_bytes > ((uint64_t)1 << 42)) return RA_ERR_SHAPE;
+  const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out;
+  if (a < b + out_bytes && b < a + in_bytes) return RA_ERR_SHAPE;
+  if (!workspace || ws_bytes < classify_doc_ws(effective_docs(cu, n_docs), cp_size, sl)) return RA_ERR_WORKSPACE;
   return RA_OK;
 }
 

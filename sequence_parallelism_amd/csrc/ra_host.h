@@ -14,8 +14,19 @@ struct Layout {
   int nqt, nkt;    // tiles along the local query / key index
   int wl_stride;   // work-list entries reserved per query tile (cp * nkt)
   int n_docs_dev;  // documents the kernels see (1 = no document mask)
-  size_t cu_off, count_off, order_off, wl_off, total;
+  int doczig;      // RA_PART_DOC_ZIGZAG: cu is always uploaded, plus the block prefix and descriptors
+  int nblk;        // doc-zigzag: 64-slot blocks per rank (s_local / 64)
+  size_t cu_off, prefix_off, blk_off, count_off, order_off, wl_off, total;
 };
+
+// Tokens (slots) each rank holds: s_total / cp, or for RA_PART_DOC_ZIGZAG the
+// padded per-document pieces (cu NULL: one document). Also fills the per-document
+// block prefix [n_docs + 1] when `prefix` is non-NULL. Returns -1 on overflow.
+int64_t local_len(const ra_shape* shape, int32_t cp_size, int32_t partition, const int32_t* cu, int32_t n_docs,
+                  int32_t* prefix);
+
+// Upper bound of local_len over every cu_seqlens with n_docs documents.
+int64_t local_len_bound(const ra_shape* shape, int32_t cp_size, int32_t n_docs);
 
 // Workspace of ra_backward: the forward's plan (dQ kernel), the key-side plan
 // of the dK/dV kernel, and the per-row sums D = dO . O.
@@ -33,11 +44,13 @@ ra_status check_shape(const ra_shape* shape, int32_t cp_size, int32_t rank, int3
 // cu_seqlens checks: NULL is one document; otherwise 0 = c0 < c1 < ... < c_n = s_total.
 ra_status check_cu(const int32_t* cu, int32_t n_docs, int64_t s_total);
 
-// Workspace layout of ra_forward / ra_forward_steps for a validated shape.
-Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev);
+// Workspace layout of the attention entry points for a validated shape, given the
+// local length (local_len) and the partition.
+Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition, int64_t s_local);
 
 // Workspace layout of ra_backward for a validated shape.
-BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev);
+BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition,
+                     int64_t s_local);
 
 // Full validation of ra_backward arguments.
 ra_status check_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -88,6 +101,11 @@ UspLayout usp_layout(const ra_shape* shape, int32_t ulysses, int32_t ring, int32
 ra_status check_usp(const void* q, const void* k, const void* v, const int32_t* cu, int32_t n_docs, int32_t ulysses,
                     int32_t ring, int32_t partition, const ra_shape* shape, const void* out, const float* lse,
                     const void* workspace, size_t ws_bytes);
+
+// cp_reorder_docs: tensors, shape and documents (the reorder of RA_PART_DOC_ZIGZAG).
+ra_status check_cp_reorder_docs(const void* in, const void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
+                                int32_t cp_size, const int32_t* cu, int32_t n_docs, int32_t inverse,
+                                const void* workspace, size_t ws_bytes);
 
 ra_status check_cp_reorder(const void* in, const void* out, int64_t s, int32_t h, int32_t d, int32_t elem_bytes,
                            int32_t cp_size, int32_t partition, int32_t inverse);

@@ -30,9 +30,20 @@ hipError_t launch_ring_attn(const AttnArgs& a, int d, int in_bf16, int out_bf16,
 hipError_t launch_upload_i32(const int32_t* host, int n, int32_t* dst, hipStream_t st);
 
 // Work list of non-SKIP (step, key tile) entries per query tile, and the tile order by work.
-hipError_t launch_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
-                           int causal, int bm, int bn, int nqt, int nkt, int wl_stride, int* wl, int* wl_count,
-                           int* order, hipStream_t st);
+hipError_t launch_worklist(const int* cu, const int2* blk, int n_docs, int s_total, int s_local, int cp, int rank,
+                           int part, int causal, int bm, int bn, int nqt, int nkt, int wl_stride, int* wl,
+                           int* wl_count, int* order, hipStream_t st);
+
+// Doc-zigzag block descriptors [cp][nblk] from device cu_seqlens [n_docs+1] and the
+// per-document block prefix [n_docs+1] (blocks per rank before document j).
+hipError_t launch_doc_blocks(const int* cu, const int* prefix, int n_docs, int cp, int nblk, int2* blk,
+                             hipStream_t st);
+
+// Doc-zigzag CP reorder: forward [s][row] -> [cp][s_local][row] (padding rows zero);
+// inverse [cp][s_local][row] -> [s][row].
+hipError_t launch_cp_reorder_docs(const void* in, void* out, int64_t s, int64_t row_bytes, int cp, int s_local,
+                                  const int* cu, const int* prefix, const int2* blk, int n_docs, int inverse,
+                                  hipStream_t st);
 
 // Orders n tiles by descending count (ties by index) into order[0..n).
 hipError_t launch_order(const int* count, int n, int* order, hipStream_t st);
@@ -40,8 +51,8 @@ hipError_t launch_order(const int* count, int n, int* order, hipStream_t st);
 // Key-side work list of the dK/dV kernels: for key tile kt = s * nkt + J (keys
 // [J bk, (J+1) bk) of chunk s), the non-SKIP query tiles of `rank`; then the
 // heaviest-first key-tile order.
-hipError_t launch_kv_worklist(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
-                              int causal, int bq, int bk, int nqt, int nkt, int stride, int* wl, int* count,
+hipError_t launch_kv_worklist(const int* cu, const int2* blk, int n_docs, int s_total, int s_local, int cp, int rank,
+                              int part, int causal, int bq, int bk, int nqt, int nkt, int stride, int* wl, int* count,
                               int* order, hipStream_t st);
 
 // dsum[h][i] = sum_c dout[i][h][c] * out[i][h][c] (fp32).
@@ -51,8 +62,8 @@ hipError_t launch_bwd_dsum(const void* out, const void* dout, float* dsum, int r
 // dQ kernel then dK/dV kernel.
 hipError_t launch_ring_bwd(const BwdArgs& a, int d, int in_bf16, hipStream_t st);
 
-hipError_t launch_classify(const int* cu, int n_docs, int s_total, int s_local, int cp, int rank, int part,
-                           int causal, int bm, int bn, int nqt, int nkt, int8_t* cls, hipStream_t st);
+hipError_t launch_classify(const int* cu, const int2* blk, int n_docs, int s_total, int s_local, int cp, int rank,
+                           int part, int causal, int bm, int bn, int nqt, int nkt, int8_t* cls, hipStream_t st);
 
 hipError_t launch_lse_merge(int64_t rows, int h, int d, const float* o_a, const float* lse_a, const float* o_b,
                             const float* lse_b, float* o_out, float* lse_out, hipStream_t st);

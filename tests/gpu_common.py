@@ -30,14 +30,21 @@ def device_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().cpu().numpy()
 
 
+def reorder(x: torch.Tensor, cp: int, partition: str, cu_seqlens=None) -> torch.Tensor:
+    """Global [S,h,d] -> rank-major [cp,S_l,h,d] with the GPU reorder kernels."""
+    if partition == "doc_zigzag":
+        return ra.cp_reorder_docs(x, cp, cu_seqlens)
+    return ra.cp_reorder(x, cp, partition)
+
+
 def rank_inputs(g: synth.GlobalInputs, cp: int, rank: int, partition: str):
-    """Global Q/K/V -> (q of `rank` [S_l,hq,d], k/v [cp,S_l,hkv,d]) with the GPU cp_reorder kernel."""
+    """Global Q/K/V -> (q of `rank` [S_l,hq,d], k/v [cp,S_l,hkv,d]) with the GPU reorder kernels."""
     q = to_device(g.q, g.dtype)
     k = to_device(g.k, g.dtype)
     v = to_device(g.v, g.dtype)
-    qr = ra.cp_reorder(q, cp, partition)[rank].contiguous()
-    kr = ra.cp_reorder(k, cp, partition)
-    vr = ra.cp_reorder(v, cp, partition)
+    qr = reorder(q, cp, partition, g.cu_seqlens)[rank].contiguous()
+    kr = reorder(k, cp, partition, g.cu_seqlens)
+    vr = reorder(v, cp, partition, g.cu_seqlens)
     return qr, kr, vr
 
 

@@ -66,7 +66,7 @@ def test_forward_validation_codes():
     assert fwd(shape(softmax_scale=float("nan"))) == ra.RA_ERR_SHAPE
     assert fwd(shape(), cp=0) == ra.RA_ERR_SHAPE
     assert fwd(shape(), cp=65) == ra.RA_ERR_SHAPE
-    assert fwd(shape(), part=3) == ra.RA_ERR_UNSUPPORTED
+    assert fwd(shape(), part=4) == ra.RA_ERR_UNSUPPORTED
     assert fwd(shape(), rank=4) == ra.RA_ERR_RANK
     assert fwd(shape(), rank=-1) == ra.RA_ERR_RANK
     assert fwd(shape(hq=32, hkv=6)) == ra.RA_ERR_HEADS
@@ -83,8 +83,8 @@ def test_forward_validation_codes():
     assert need > 0
     assert fwd(sh, ws=None) == ra.RA_ERR_WORKSPACE
     assert fwd(sh, ws_bytes=256) == ra.RA_ERR_WORKSPACE
-    # ra_workspace_size covers both the merged and the per-step layouts; the per-step one is larger here
-    assert _lib().ra_forward_steps(P, P, P, None, 0, 4, 0, 1, ctypes.byref(sh), P, P, P, need - 1, None) \
+    # the per-step entry point checks its workspace too
+    assert _lib().ra_forward_steps(P, P, P, None, 0, 4, 0, 1, ctypes.byref(sh), P, P, P, 1024, None) \
         == ra.RA_ERR_WORKSPACE
 
 
@@ -179,7 +179,7 @@ def test_backward_validation_codes():
     need = ra.ra_backward_workspace_size(sh, 4, 0)
     assert need > ra.ra_workspace_size(sh, 4, 0)
     assert bwd(sh, ws=None) == ra.RA_ERR_WORKSPACE
-    assert bwd(sh, ws_bytes=need - 1) == ra.RA_ERR_WORKSPACE
+    assert bwd(sh, ws_bytes=1024) == ra.RA_ERR_WORKSPACE
     assert ra.ra_backward_workspace_size(shape(s_total=0), 4, 0) == 0
     assert _lib().ra_backward_workspace_size(None, 4, 0) == 0
     assert ra.ra_backward_workspace_size(sh, 4, 50) > need
@@ -211,3 +211,34 @@ def test_ulysses_strided_and_usp_validation():
     assert need > 0
     assert usp(sh, ws_bytes=need - 1) == ra.RA_ERR_WORKSPACE
     assert ra.usp_workspace_size(sh, 3, 2, 0) == 0
+
+
+def test_doc_zigzag_validation_and_lengths():
+    lib = _lib()
+    cu = [0, 100, 101, 333, 512]
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    # local length: every document in 2cp pieces of ceil(L/2cp) padded to 64 slots, 2 pieces per rank
+    assert ra.ra_local_length(512, 4, "doc_zigzag", cu) == 64 * 2 * 4
+    assert ra.ra_local_length(512, 4, "zigzag", cu) == 128
+    assert ra.ra_local_length(510, 4, "zigzag") == -1          # not divisible by 2cp
+    assert ra.ra_local_length(510, 4, "doc_zigzag") == 128     # one padded document: 2 * 64
+    assert ra.ra_local_length(512, 4, "doc_zigzag", [0, 600, 512]) == -1
+    assert ra.ra_doc_workspace_size(512, 4, cu) > 0
+    # plans and the planned kernel, and the Ulysses x Ring grid, do not take doc-zigzag
+    sh = shape(s_total=512, hq=2, hkv=2)
+    assert lib.ra_plan(ctypes.byref(sh), arr, 4, 4, 0, 3, P, 1 << 40, None) == ra.RA_ERR_UNSUPPORTED
+    assert lib.ra_forward_planned(P, P, P, 4, 4, 0, 3, ctypes.byref(sh), P, P, P, 1 << 40, None) \
+        == ra.RA_ERR_UNSUPPORTED
+    assert lib.usp_forward(P, P, P, arr, 4, 2, 2, 3, ctypes.byref(sh), P, P, P, 1 << 40, None) \
+        == ra.RA_ERR_UNSUPPORTED
+    assert lib.cp_reorder(P, P2, 512, 2, 128, 2, 4, 3, 0, None) == ra.RA_ERR_UNSUPPORTED
+    # doc-zigzag classification: tiles of 16..128 only, and the document tables' workspace
+    assert lib.ra_classify(ctypes.byref(sh), arr, 4, 4, 0, 3, 96, 64, P, P, 1 << 20, None) == ra.RA_ERR_UNSUPPORTED
+    assert lib.ra_classify(ctypes.byref(sh), arr, 4, 4, 0, 3, 64, 64, P, P, 64, None) == ra.RA_ERR_WORKSPACE
+    # reorder: tensors, documents and workspace
+    assert lib.cp_reorder_docs(None, P2, 512, 2, 128, 2, 4, arr, 4, 0, P, 1 << 20, None) == ra.RA_ERR_NULL
+    bad = (ctypes.c_int32 * 3)(0, 600, 512)
+    assert lib.cp_reorder_docs(P, P2, 512, 2, 128, 2, 4, bad, 2, 0, P, 1 << 20, None) == ra.RA_ERR_CU_SEQLENS
+    assert lib.cp_reorder_docs(P, P2, 512, 2, 128, 2, 4, arr, 4, 0, P, 64, None) == ra.RA_ERR_WORKSPACE
+    # the forward's workspace size covers the doc-zigzag layout
+    assert fwd(sh, cu=cu, n_docs=4, part=3, ws_bytes=ra.ra_workspace_size(sh, 4, 4) - 1, q=None) == ra.RA_ERR_NULL
