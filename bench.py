@@ -13,9 +13,11 @@ the rank), i.e. masked or skipped work is not counted.
 
 Also reported (extra "kernels" object): the attention kernel alone (HIP events
 on the launch stream) with its roofline against the bf16 MFMA peak, the
-permute / reorder / merge kernels in HBM GB/s, and the other workloads
-(Ulysses path at 131072 tokens, GQA striped, packed documents). The CPU
-oracle is timed on a bounded row sample on the host cores (rank 0 only).
+backward of the same share (ra_backward, FLOPs counted as 2.5 x the forward's),
+the permute / reorder / merge kernels in HBM GB/s, and the other workloads
+(Ulysses path at 131072 tokens, a 4 x 2 Ulysses x Ring grid, GQA striped,
+packed documents under the global zigzag and under per-document zigzag). The
+CPU oracle is timed on a bounded row sample on the host cores (rank 0 only).
 
 Runs on one GPU only: --gpus above 1 exits with a message.
 """
@@ -366,6 +368,26 @@ def extras(np, torch, ra, synth, dev, reps):
     res["ulysses_pipeline_s128k"] = {"avg_ms": tp["avg_ms"], "tflops": fl / (tp["avg_ms"] * 1e-3) / 1e12}
     del xq, xk, xv, yq, yk, yv, o_all, back
 
+    # Ulysses x Ring hybrid: a 4 x 2 grid (Ulysses 4 inside, zigzag ring of 2 across), S=131072,
+    # 32 heads; the whole grid's work on one GPU (all 8 devices' permutes and attention)
+    log("extras: Ulysses x Ring grid")
+    U, R, S = 4, 2, 131072
+    sh = S // (U * R)
+    gq, gk, gvv = randn(R, U, sh, H, d), randn(R, U, sh, H, d), randn(R, U, sh, H, d)
+    ushape = ra.make_shape(S, H, H, d, True, 0.0, ra.RA_BF16, ra.RA_BF16)
+    uws = torch.empty(ra.usp_workspace_size(ushape, U, R, 0), dtype=torch.uint8, device=dev)
+    uout = torch.empty_like(gq)
+    ulse = torch.empty((U, R, H // U, S // R), dtype=torch.float32, device=dev)
+    tu = time_events(torch, lambda: ra.usp_forward(gq, gk, gvv, None, U, R, "zigzag", out=uout, lse=ulse,
+                                                   workspace=uws), max(3, reps // 2))
+    fl = 4.0 * d * H * visible_pairs(np, "contiguous", S, 1, 0)
+    res["usp_grid_u4_r2_s128k_h32"] = {"avg_ms": tu["avg_ms"], "flops": fl,
+                                       "tflops": fl / (tu["avg_ms"] * 1e-3) / 1e12,
+                                       "per_device_ms": tu["avg_ms"] / (U * R),
+                                       "note": "whole grid: 3 x R strided Ulysses permutes, U x R ring attentions "
+                                               "(R steps each), R inverse permutes"}
+    del gq, gk, gvv, uws, uout, ulse
+
     # GQA striped: 32 q heads / 8 kv heads, S=65536, CP=8, rank 0
     log("extras: GQA striped")
     w = synth.GQA_STRIPED
@@ -395,6 +417,30 @@ def extras(np, torch, ra, synth, dev, reps):
                          "tflops": fl / (tr["avg_ms"] * 1e-3) / 1e12})
     heavy = max(per_rank, key=lambda x: x["flops"])
     res["ring_attn_packed_docs_zigzag"] = {"n_docs": len(cu) - 1, "max_work_rank": heavy, "ranks": per_rank}
+    del q_all, k, v
+
+    # the same documents under per-document zigzag: every rank holds two pieces of every
+    # document (padded to 64-slot blocks), so the ranks' work is even; timed with ra_forward
+    # (plan included: the planned entry point does not take this partition)
+    log("extras: packed documents, per-document zigzag")
+    sld = ra.ra_local_length(w.s_total, w.cp, "doc_zigzag", cu)
+    q_all = randn(w.cp, sld, w.hq, w.d)
+    k, v = randn(w.cp, sld, w.hkv, w.d), randn(w.cp, sld, w.hkv, w.d)
+    dshape = ra.make_shape(w.s_total, w.hq, w.hkv, w.d, True, 0.0, ra.RA_BF16, ra.RA_BF16)
+    dws = torch.empty(ra.ra_workspace_size(dshape, w.cp, len(cu) - 1), dtype=torch.uint8, device=dev)
+    dout = torch.empty((sld, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((w.hq, sld), dtype=torch.float32, device=dev)
+    per_rank_d = []
+    for r in range(w.cp):
+        tr = time_events(torch, lambda: ra.ra_forward(q_all[r], k, v, cu, w.cp, r, "doc_zigzag", out=dout, lse=dlse,
+                                                      workspace=dws), max(3, reps // 2))
+        per_rank_d.append({"rank": r, "avg_ms": tr["avg_ms"]})
+    slowest = max(per_rank_d, key=lambda x: x["avg_ms"])
+    total_fl = 4.0 * w.d * w.hq * visible_pairs(np, "contiguous", w.s_total, 1, 0, cu)
+    res["ring_attn_packed_docs_doc_zigzag"] = {
+        "n_docs": len(cu) - 1, "s_local": sld, "s_local_unpadded": slp, "slowest_rank": slowest, "ranks": per_rank_d,
+        "slowest_rank_speedup_vs_global_zigzag": max(x["avg_ms"] for x in per_rank) / slowest["avg_ms"],
+        "tflops_all_ranks": total_fl / (sum(x["avg_ms"] for x in per_rank_d) * 1e-3) / 1e12}
 
     # measured copy ceiling: torch's device-to-device copy of 1 GiB
     src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
