@@ -105,7 +105,7 @@ def traffic_from_profiles(kernel_src_sha):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("ra_attn.hip", "ra_common.h", "ra_internal.h"):
+    for f in ("ra_attn.hip", "ra_common.h", "ra_device.h", "ra_internal.h"):
         h.update(open(os.path.join(ROOT, "sequence_parallelism_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
@@ -148,7 +148,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows-every", type=int, default=16)
+    ap.add_argument("--cpu-rows-every", type=int, default=4)
     ap.add_argument("--mode", default="full", choices=["full", "attn-only", "bwd-only", "copy-only"],
                     help="attn-only / copy-only: a few launches of one kernel, for counter runs")
     args = ap.parse_args()
