@@ -96,7 +96,7 @@ def traffic_from_profiles(kernel_src_sha):
     if not os.path.exists(path):
         return None
     txt = open(path).read()
-    m_sha = re.search(r"kernel source sha256:\s*([0-9a-f]{64})", txt)
+    m_sha = re.search(r"[Kk]ernel source sha256[^:]*:\s*([0-9a-f]{64})", txt)
     m_b = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", txt)
     if not m_sha or not m_b or m_sha.group(1) != kernel_src_sha:
         return None
