@@ -75,9 +75,10 @@ ra_status upload_docs(const Layout& L, const int32_t* cu, int32_t nd, int32_t cp
   return RA_OK;
 }
 
-ra_status run_plan(const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition, const ra_shape* shape,
-                   void* workspace, hipStream_t st) {
-  const Layout L = layout_for(shape, cp, partition, cu, nd);
+// Uploads the document tables and builds the work list and tile order for the
+// query tiles of layout L.
+ra_status run_plan(const Layout& L, const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition,
+                   const ra_shape* shape, void* workspace, hipStream_t st) {
   char* ws = (char*)workspace;
   const ra_status u = upload_docs(L, cu, nd, cp, partition, shape, ws, st);
   if (u != RA_OK) return u;
@@ -88,6 +89,12 @@ ra_status run_plan(const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int3
                       (int*)(ws + L.order_off), st) != hipSuccess)
     return RA_ERR_HIP;
   return RA_OK;
+}
+
+// The same for the forward kernel's tile height.
+ra_status run_plan(const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition, const ra_shape* shape,
+                   void* workspace, hipStream_t st) {
+  return run_plan(layout_for(shape, cp, partition, cu, nd), cu, nd, cp, rank, partition, shape, workspace, st);
 }
 
 ra_status run_attention(const void* q, const void* k, const void* v, const Layout& L, int32_t nd, int32_t cp,
@@ -132,7 +139,7 @@ ra_status run_backward(const void* q, const void* k, const void* v, const void* 
   const BwdLayout B = bwd_layout(shape, cp, nd, partition, local_len(shape, cp, partition, cu, nd, nullptr));
   const Layout& L = B.fwd;
   char* ws = (char*)workspace;
-  const ra_status p = run_plan(cu, nd, cp, rank, partition, shape, workspace, st);
+  const ra_status p = run_plan(L, cu, nd, cp, rank, partition, shape, workspace, st);
   if (p != RA_OK) return p;
   const int* dcu = nd > 1 ? (const int*)(ws + L.cu_off) : nullptr;
   const int2* blk = L.doczig ? (const int2*)(ws + L.blk_off) : nullptr;

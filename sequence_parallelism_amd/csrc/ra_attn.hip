@@ -188,15 +188,17 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
     }
   };
 
+  ListWindow wl;
+  wl.init(list, n_ent, lane);
   int cur_t = 0;
   if (n_ent > 0) {
-    load_tile(list[0], 0);
+    load_tile(wl.get(0), 0);
     store_tile(0);
   }
   __syncthreads();
 
   for (int e = 0; e < n_ent; ++e) {
-    const int ent = list[e];
+    const int ent = wl.get(e);
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
     const bool ent_ok = t < a.cp && J < a.nkt && cls != CLS_SKIP;
     if constexpr (STEPS) {
@@ -206,7 +208,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
         ++cur_t;
       }
     }
-    if (e + 1 < n_ent) load_tile(list[e + 1], (e + 1) & 1);
+    if (e + 1 < n_ent) load_tile(wl.get(e + 1), (e + 1) & 1);
 
     const int ka = J * BN;
     const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
@@ -298,6 +300,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
 
     if (e + 1 < n_ent) store_tile((e + 1) & 1);
     __syncthreads();
+    wl.advance(e, lane);
   }
 
   if constexpr (STEPS) {
@@ -377,9 +380,11 @@ __global__ void __launch_bounds__(64) ring_attn_f32_kernel(const AttnArgs a) {
     }
   };
   int cur_t = 0;
+  ListWindow wl;
+  wl.init(list, n_ent, lane);
 
-  for (int e = 0; e < n_ent; ++e) {
-    const int ent = list[e];
+  for (int e = 0; e < n_ent; wl.advance(e, lane), ++e) {
+    const int ent = wl.get(e);
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
     if (t >= a.cp || J >= a.nkt || cls == CLS_SKIP) continue;  // uniform across the block
     const int owner = ring_owner(a.rank, t, a.cp);
@@ -475,10 +480,7 @@ static hipError_t launch_f32(const AttnArgs& a, hipStream_t st) {
 hipError_t launch_ring_attn(const AttnArgs& a, int d, int in_bf16, int out_bf16, int steps, hipStream_t st) {
   if (a.nqt == 0 || a.hq == 0) return hipSuccess;
   if (in_bf16) {
-    if (d == 128) {
-      if (steps) return launch_bf16<128, false, true>(a, st);
-      return out_bf16 ? launch_bf16<128, true, false>(a, st) : launch_bf16<128, false, false>(a, st);
-    }
+    if (d == 128) return launch_ring_attn_pp(a, out_bf16, steps, st);
     if (d == 64) {
       if (steps) return launch_bf16<64, false, true>(a, st);
       return out_bf16 ? launch_bf16<64, true, false>(a, st) : launch_bf16<64, false, false>(a, st);

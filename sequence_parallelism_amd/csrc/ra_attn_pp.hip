@@ -1,0 +1,419 @@
+// Ring-step attention for bf16 inputs with head_dim 128: a two-group
+// ("ping-pong") schedule for gfx950.
+//
+// It computes what the generic bf16 kernel computes (the FlashAttention-style
+// block of the Sequence Parallelism concept page, section 二, per key tile of
+// the work list: S = Q K^T, mask on global positions, online softmax with the
+// exact running max, O += P V, and the LSE of each row), with the same
+// transposed MFMA mapping (S^T = K Q^T and O^T = V^T P^T on
+// v_mfma_f32_32x32x16_bf16, P^T from the score accumulator converted in place,
+// V^T through ds_read_b64_tr_b16). What differs is how the work is scheduled.
+//
+// One workgroup of 8 waves owns 256 query rows of one head; wave w owns rows
+// 32 w .. 32 w + 31, so waves 0-3 (group 0) hold rows [0, 128) and waves 4-7
+// (group 1) rows [128, 256), and waves w and w + 4 share a SIMD. For key tile
+// e a wave runs two phases:
+//   M(e)  matrix products: S(e) = K(e) Q^T and O += V(e-1)^T P(e-1)
+//   V(e)  online softmax of S(e) into P(e) (vector ALU and exp)
+// in the order M(0) V(0) M(1) ... V(n-1) M(n). A workgroup barrier ends every
+// phase, and group 1 runs one phase behind group 0, so while one wave of a
+// SIMD issues MFMAs the other runs its softmax, and they swap at each barrier.
+// One workgroup per CU (96 KiB of LDS) keeps two waves per SIMD.
+//
+// Key and value tiles arrive by direct global->LDS loads, three LDS stages of
+// each. In V(e), group 0 loads K(e+2) and group 1 loads V(e+2); each wave waits
+// for its own loads two phases later, just before the barrier that publishes
+// them (K(e) is read in slots 2e and 2e+1, V(e) in slots 2e+2 and 2e+3; slot s
+// is phase s of group 0 and phase s-1 of group 1). The loads are written in
+// inline assembly: the compiler would otherwise order every transposing LDS
+// read after all outstanding direct loads, and the barrier here is a bare
+// s_barrier after an LDS-only wait for the same reason (a __syncthreads fence
+// also waits for every outstanding load); both waits are counted by hand.
+#include "ra_common.h"
+#include "ra_device.h"
+#include "ra_internal.h"
+
+namespace ra {
+
+namespace {
+
+constexpr int kPpD = 128;
+constexpr int kPpBM = kAttnBf16D128BM;  // 256 query rows per workgroup
+constexpr int kPpBN = kAttnBf16BN;      // 64 keys per tile
+constexpr int kPpStages = 3;
+constexpr int kPpTile = kPpBN * kPpD;  // elements of one K or V tile (16 KiB)
+
+// All 8 waves meet; the LDS reads issued before have returned (the direct
+// loads of the next phase may overwrite what they read).
+__device__ __forceinline__ void pp_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Waits until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void pp_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from buffer r at byte offset voff into LDS: lane L writes
+// LDS bytes [lds + 16 L, lds + 16 L + 16). lds is wave-uniform. No register
+// results, so nothing is left for the compiler to wait on.
+__device__ __forceinline__ void pp_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// Pins x in registers at this point of the program (an empty asm that reads
+// and rewrites it): the code computing x runs before later volatile asm, the
+// phase barrier included. Without it the optimiser sinks the softmax below the
+// barrier that ends its phase, next to the products that consume P, and the
+// two groups' vector and matrix work no longer alternate.
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+__device__ __forceinline__ bool entry_ok(int ent, const AttnArgs& a) {
+  return wl_step(ent) < a.cp && wl_tile(ent) < a.nkt && wl_cls(ent) != CLS_SKIP;
+}
+
+}  // namespace
+
+template <bool OUT_BF16, bool STEPS>
+__global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) {
+  constexpr int D = kPpD, BM = kPpBM, BN = kPpBN;
+  constexpr int NCT = D / 32;  // 32-wide output column tiles
+  constexpr int NKD = D / 16;  // 16-deep reduction steps over d
+  // LDS: K tile row r, 16-byte chunk c at chunk slot c ^ (r & 15) (16-byte reads
+  // down 16 rows); V tile chunk c of row r at c ^ 4 (r & 3) (transposing reads of
+  // 4 rows x 4 chunks). Neither read has bank conflicts.
+  __shared__ __attribute__((aligned(1024))) __bf16 kbuf[kPpStages][kPpTile];
+  __shared__ __attribute__((aligned(1024))) __bf16 vbuf[kPpStages][kPpTile];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
+  const int grp = wave >> 2, wq = wave & 3;
+  const int hi32 = lane >> 5, l32 = lane & 31;
+  const int qt = a.order[blockIdx.x / a.hq];
+  if (qt < 0 || qt >= a.nqt) return;  // plan made for other arguments: nothing safe to do
+  const int h = head_of_slot(blockIdx.x % a.hq, a.hq);
+  const int g = h / (a.hq / a.hkv);
+  const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
+  const int row = qt * BM + wave * 32 + l32;
+  const bool row_ok = row < a.s_local;
+  const float C = a.scale_log2;
+
+  // Q^T operand: lane holds q[row][16 j + 8 hi32 + 0..7]; rows past the end read 0.
+  bf16x8 qreg[NKD];
+  {
+    const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(a.q, (uint32_t)a.s_local * a.hq * D * 2u);
+    const uint32_t qoff = ((uint32_t)row * a.hq + h) * D * 2u + 16u * hi32;
+#pragma unroll
+    for (int j = 0; j < NKD; ++j) qreg[j] = __builtin_bit_cast(bf16x8, buffer_load16(qr, qoff + 32u * j));
+  }
+  int lo = 1, hi = 0;  // empty interval for rows past the end
+  if (row_ok) row_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, a.rank, row), lo, hi);
+
+  f32x16 acc[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
+  float m = -INFINITY, l = 0.f;  // running max (log2 units) and sum of P
+  bf16x8 pb[4];  // P^T(e) in bf16: from V(e) to M(e+1)
+
+  const uint32_t kv_row_bytes = (uint32_t)a.hkv * D * 2u;
+  const uint32_t chunk_bytes = (uint32_t)a.s_local * kv_row_bytes;
+  const int n = clamp_count(a.wl_count[qt], a.wl_stride);
+  ListWindow wl;
+  wl.init(a.wl + (size_t)qt * a.wl_stride, n, lane);
+
+  // Direct loads: wave wq of a group fills rows 16 wq .. 16 wq + 15 of a tile,
+  // 4 rows per instruction; lane L lands in chunk slot L % 16 of row L / 16 and
+  // fetches the chunk that the swizzle maps there (group 0: K, group 1: V).
+  uint32_t d_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wq + 4 * i + (lane >> 4), pc = lane & 15;
+    const int chunk = grp ? (pc ^ (4 * (r & 3))) : (pc ^ (r & 15));
+    d_off[i] = (uint32_t)r * kv_row_bytes + ((uint32_t)g * D + 8 * chunk) * 2u;
+  }
+  const uint32_t lds_k = (uint32_t)(size_t)(__attribute__((address_space(3))) __bf16*)&kbuf[0][0];
+  const uint32_t lds_v = (uint32_t)(size_t)(__attribute__((address_space(3))) __bf16*)&vbuf[0][0];
+  const uint32_t lds_mine = (grp ? lds_v : lds_k) + 4096u * wq;
+  const void* src_mine = grp ? a.v : a.k;
+  // This group's tile of entry idx (list value ent) into stage idx % 3 (4 instructions).
+  auto issue = [&](int idx, int ent) {
+    const size_t cbase = (size_t)ring_owner(a.rank, wl_step(ent), a.cp) * chunk_bytes;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc((const char*)src_mine + cbase, chunk_bytes);
+    const uint32_t toff = (uint32_t)wl_tile(ent) * BN * kv_row_bytes;
+    const uint32_t base = lds_mine + (uint32_t)(idx % kPpStages) * (kPpTile * 2u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp_dma16(r, toff + d_off[i], base + 1024u * i);
+  };
+
+  // Per-lane LDS element offsets inside a tile at key half kt = 0, j = 0 / jj = 0:
+  //   k_off[j]  row l32, logical chunk 2 j + hi32 (A operand of S^T); +32 rows for kt = 1
+  //   v_off[c]  transposing read of rows 4 hi32 + (lane % 16) / 4 (and +8), columns
+  //             32 c + 16 ((lane / 16) % 2) + 4 (lane % 4) (A operand of O^T)
+  int k_off[NKD], v_off[NCT];
+#pragma unroll
+  for (int j = 0; j < NKD; ++j) k_off[j] = l32 * D + 8 * ((2 * j + hi32) ^ (l32 & 15));
+  {
+    const int r0 = 4 * hi32 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      v_off[c] = r0 * D + (c0 ^ (32 * (r0 & 3)));
+    }
+  }
+
+  // M phase parts: S^T(e) = K(e) Q^T into sc, and O^T += V(e-1)^T P^T(e-1).
+  auto qk = [&](int e, f32x16 (&sc)[2]) {
+    const __bf16* ks = kbuf[e % kPpStages];
+    int ko[NKD];
+#pragma unroll
+    for (int j = 0; j < NKD; ++j) ko[j] = opaque(k_off[j]);
+#pragma unroll
+    for (int j = 0; j < NKD; ++j)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 ka8 = *(const bf16x8*)(ks + ko[j] + kt * 32 * D);
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka8, qreg[j], j ? sc[kt] : f32x16{}, 0, 0, 0);
+      }
+  };
+  auto pv = [&](int e) {
+    const __bf16* vs = vbuf[e % kPpStages];
+    int vo[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) vo[c] = opaque(v_off[c]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const __bf16* p = vs + vo[c] + (kt * 32 + jj * 16) * D;
+          const bf16x8 va = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 8 * D), 0, 1, 2, 3, 4, 5, 6, 7);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[2 * kt + jj], acc[c], 0, 0, 0);
+        }
+  };
+
+  // normalised partial of the current state (steps mode)
+  auto flush = [&](int t) {
+    const float lt = swap_half_sum(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row_ok) {
+      float* op = a.o_steps + ((size_t)t * a.s_local * a.hq + (size_t)row * a.hq + h) * D;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int col = c * 32 + 8 * i4 + 4 * hi32;
+          *(f32x4*)(op + col) = f32x4{acc[c][4 * i4], acc[c][4 * i4 + 1], acc[c][4 * i4 + 2], acc[c][4 * i4 + 3]} *
+                                inv;
+        }
+      if (hi32 == 0)
+        a.lse_steps[(size_t)t * a.hq * a.s_local + (size_t)h * a.s_local + row] =
+            lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    }
+  };
+  auto reset = [&]() {
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[c] = f32x16{};
+    m = -INFINITY;
+    l = 0.f;
+  };
+  int cur_t = 0;
+
+  // Issue order of a full M phase (16 K reads, 16 MFMAs of S, 32 transposing V
+  // reads, 16 MFMAs of O): the LDS reads run about 8 ahead of the MFMAs that use
+  // them, and the V reads start under the last MFMAs of S.
+  auto m_order = [&]() {
+    constexpr int kDsRead = 0x100, kMfma = 0x008;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, 6, 0);
+  };
+
+  // V phase: online softmax of S^T(e) into P^T(e). An entry that fails the range
+  // checks is a fully masked tile (P = 0, state unchanged).
+  auto v_phase = [&](int e, f32x16 (&sc)[2]) {
+    const int ent = wl.get(e);
+    const bool ok = entry_ok(ent, a);
+    const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
+    if constexpr (STEPS) {
+      while (ok && cur_t < t) {
+        flush(cur_t);
+        reset();
+        ++cur_t;
+      }
+    }
+    {
+      const int ka = J * BN;
+      const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
+      bool need_mask = !ok || kb - ka < BN || cls == CLS_PARTIAL;
+      TileMask tm{0, 0, 0, 0};
+      if (ok && need_mask) {
+        tm = tile_mask(pinfo, ring_owner(a.rank, t, a.cp), ka, kb, cls, row_ok, lo, hi);
+        need_mask = !__all(tile_all_visible(tm, BN) || !row_ok);
+      }
+      // lane holds keys n = 32 kt + 8 (i/4) + 4 hi32 + (i%4) of its row
+      if (need_mask) {
+        const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int nk = kt * 32 + 8 * (i >> 2) + (i & 3);
+            const bool vis = ((unsigned)(nk + ba) < (unsigned)tm.la) | ((unsigned)(nk + bb) < (unsigned)tm.lb);
+            sc[kt][i] = vis ? sc[kt][i] : -INFINITY;
+          }
+      }
+      // online softmax in the log2 domain; the running max is exact
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
+      mx = swap_half_max(mx) * C;
+      // rows that do not grow keep alpha = 1 exactly (their m may still be -inf)
+      const bool grow = mx > m;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+      m = grow ? mx : m;
+      const float m_use = m == -INFINITY ? 0.f : m;
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][i], C, -m_use));
+          sc[kt][i] = p;
+          rs += p;
+        }
+      l = __builtin_fmaf(l, alpha, rs);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        pb[2 * kt] = __builtin_convertvector(sc[kt].lo, bf16x8);
+        pb[2 * kt + 1] = __builtin_convertvector(sc[kt].hi, bf16x8);
+      }
+      // The accumulator is rescaled last: it is the destination of the products
+      // issued at the end of the previous phase, which may still be in the MFMA
+      // pipe behind the other wave's products when this phase starts.
+      if (__any(grow)) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) acc[c] *= alpha;
+      }
+    }
+  };
+
+  if (n > 0) {
+    // prologue: group 0 loads K(0), K(1) and publishes K(0); group 1 loads V(0)
+    if (grp == 0) {
+      issue(0, wl.get(0));
+      if (n > 1) {
+        issue(1, wl.get(1));
+        pp_wait_vm<4>();
+      } else {
+        pp_wait_vm<0>();
+      }
+    } else {
+      issue(0, wl.get(0));
+    }
+    pp_barrier();
+    if (grp == 1) {  // slot 0: group 1 has no phase yet; it loads V(1)
+      if (n > 1) issue(1, wl.get(1));
+      pp_barrier();
+    }
+    for (int e = 0; e < n; ++e) {
+      // M(e)
+      f32x16 sc[2];
+      __builtin_amdgcn_s_setprio(1);
+      if (e > 0) {
+        qk(e, sc);
+        pv(e - 1);
+        m_order();
+      } else {
+        qk(e, sc);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 1) {  // V(e) must have landed; V(e+1) may still be in flight
+        if (e + 1 < n) pp_wait_vm<4>();
+        else pp_wait_vm<0>();
+      }
+      pp_barrier();
+      // V(e)
+      v_phase(e, sc);
+      const bool more = e + 2 < n;
+      const int next_ent = more ? wl.get(e + 2) : 0;
+      // a list refill (every 64 entries) is waited for here, which also waits for
+      // this wave's tile loads in flight: group 0 needs K(e+1) now anyway
+      wl.advance(e, lane);
+      if (more) issue(e + 2, next_ent);
+      if (grp == 0) {  // K(e+1) must have landed; K(e+2) may still be in flight
+        if (more) pp_wait_vm<4>();
+        else pp_wait_vm<0>();
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pin(pb[k]);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) pin(acc[c]);
+      pin(l);
+      pin(m);
+      pp_barrier();
+    }
+    // M(n): the last product
+    __builtin_amdgcn_s_setprio(1);
+    pv(n - 1);
+    __builtin_amdgcn_s_setprio(0);
+    pp_barrier();
+    if (grp == 0) pp_barrier();  // last slot: group 1's M(n)
+  }
+
+  if constexpr (STEPS) {
+    while (cur_t < a.cp) {
+      flush(cur_t);
+      reset();
+      ++cur_t;
+    }
+  } else {
+    const float lt = swap_half_sum(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (row_ok) {
+      const size_t base = ((size_t)row * a.hq + h) * D;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int col = c * 32 + 8 * i4 + 4 * hi32;
+          f32x4 o4 = {acc[c][4 * i4] * inv, acc[c][4 * i4 + 1] * inv, acc[c][4 * i4 + 2] * inv,
+                      acc[c][4 * i4 + 3] * inv};
+          if constexpr (OUT_BF16) {
+            *(bf16x4*)((__bf16*)a.out + base + col) = __builtin_convertvector(o4, bf16x4);
+          } else {
+            *(f32x4*)((float*)a.out + base + col) = o4;
+          }
+        }
+      if (hi32 == 0)
+        a.lse[(size_t)h * a.s_local + row] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+hipError_t launch_ring_attn_pp(const AttnArgs& a, int out_bf16, int steps, hipStream_t st) {
+  const unsigned grid = (unsigned)a.nqt * (unsigned)a.hq;
+  if (steps)
+    hipLaunchKernelGGL((ring_attn_pp_kernel<false, true>), dim3(grid), dim3(512), 0, st, a);
+  else if (out_bf16)
+    hipLaunchKernelGGL((ring_attn_pp_kernel<true, false>), dim3(grid), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((ring_attn_pp_kernel<false, false>), dim3(grid), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -35,6 +35,7 @@ hipError_t launch_upload_i32(const int32_t* host, int n, int32_t* dst, hipStream
 // ---------------------------------------------------------------------------
 // Work list: for query tile I, every (ring step t, key tile J) whose class is
 // not SKIP, in step-major order, packed with its class. One block per tile.
+// A tile is FULL when all its 128-row parts are, SKIP when all are.
 // ---------------------------------------------------------------------------
 struct WlArgs {
   const int* cu;
@@ -63,7 +64,16 @@ __global__ void __launch_bounds__(256) worklist_kernel(const WlArgs w) {
       const int owner = (w.rank - t + w.cp) % w.cp;
       const int ka = J * w.bn;
       const int kb = ka + w.bn < w.s_local ? ka + w.bn : w.s_local;
-      c = classify_tile(p, w.rank, qa, qb, owner, ka, kb, w.cu, w.n_docs, w.s_total, w.causal);
+      // tiles taller than 128 rows: merge the classes of their 128-row parts (a
+      // part's rows form at most two runs under every partition)
+      bool any = false, all = true;
+      for (int pa = qa; pa < qb; pa += 128) {
+        const int pb = pa + 128 < qb ? pa + 128 : qb;
+        const int cp = classify_tile(p, w.rank, pa, pb, owner, ka, kb, w.cu, w.n_docs, w.s_total, w.causal);
+        any |= cp != CLS_SKIP;
+        all &= cp == CLS_FULL;
+      }
+      c = !any ? CLS_SKIP : all ? CLS_FULL : CLS_PARTIAL;
     }
     const unsigned long long bal = __ballot(c != CLS_SKIP);
     const int below = __popcll(bal & ((1ull << lane) - 1ull));

@@ -218,17 +218,19 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
     tr1_off[c] = (r0 + 8) * ROW + (DMA ? ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7)) : c0);
   }
 
+  ListWindow wl;
+  wl.init(list, n_ent, lane);
   if (n_ent > 0) {
-    load_tile(list[0], 0);
+    load_tile(wl.get(0), 0);
     store_tile(0);
   }
   __syncthreads();
 
   for (int e = 0; e < n_ent; ++e) {
-    const int ent = list[e];
+    const int ent = wl.get(e);
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
     const bool ent_ok = t < a.cp && J < a.nkt && cls != CLS_SKIP;
-    if (e + 1 < n_ent) load_tile(list[e + 1], (e + 1) & 1);
+    if (e + 1 < n_ent) load_tile(wl.get(e + 1), (e + 1) & 1);
 
     const int ka = J * BN;
     const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
@@ -297,6 +299,7 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
 
     if (e + 1 < n_ent) store_tile((e + 1) & 1);
     __syncthreads();
+    wl.advance(e, lane);
   }
 
   if (row_ok) {
@@ -391,9 +394,7 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
   }
   uint4 rq[DMA ? 1 : PER], ro[DMA ? 1 : PER];
   float rl = INFINITY, rd = 0.f;  // wave 0: LSE * log2 e and D of row `lane` of the next tile
-  auto load_tile = [&](int it, int buf) {
-    const int hh = it / n_ent;
-    const int ent = list[it - hh * n_ent];
+  auto load_tile = [&](int hh, int ent, int buf) {
     const int h = g * G + hh, I = wl_tile(ent);
     const uint32_t toff = (uint32_t)I * BQ * q_row_bytes + (uint32_t)h * D * 2u;
     if constexpr (DMA) {
@@ -462,17 +463,22 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
     tr1_off[c] = (r0 + 8) * ROW + (DMA ? ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7)) : c0);
   }
 
+  ListWindow wl;
+  wl.init(list, n_ent, lane);
   if (total > 0) {
-    load_tile(0, 0);
+    load_tile(0, wl.get(0), 0);
     store_tile(0);
   }
   __syncthreads();
 
+  // iteration it = hh * n_ent + idx: query head g G + hh, list entry idx
+  int hh = 0, idx = 0;
   for (int it = 0; it < total; ++it) {
-    const int ent = list[it % n_ent];
+    const int ent = wl.get(idx);
     const int I = wl_tile(ent), cls = wl_cls(ent);
     const bool ent_ok = I < a.nqt_kv && cls != CLS_SKIP;
-    if (it + 1 < total) load_tile(it + 1, (it + 1) & 1);
+    const bool wrap = idx + 1 == n_ent;
+    if (it + 1 < total) load_tile(wrap ? hh + 1 : hh, wl.get(wrap ? 0 : idx + 1), (it + 1) & 1);
 
     const int qa = I * BQ;
     const int qb = qa + BQ < a.s_local ? qa + BQ : a.s_local;
@@ -557,6 +563,14 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
 
     if (it + 1 < total) store_tile((it + 1) & 1);
     __syncthreads();
+    if (wrap) {
+      wl.restart(lane);
+      idx = 0;
+      ++hh;
+    } else {
+      wl.advance(idx, lane);
+      ++idx;
+    }
   }
 
   if (key_ok) {

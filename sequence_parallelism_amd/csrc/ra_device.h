@@ -25,6 +25,59 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // each row land in distinct 64-byte groups), so neither read has bank conflicts.
 __device__ __forceinline__ int swz_rt(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
+// x, hidden from the optimiser (an empty asm that reads and rewrites the
+// register). Uses: per-phase LDS addresses built from it are not split into
+// loop-invariant parts hoisted into registers; and a freshly loaded register
+// passed through it is waited for at that point, so no load stays pending
+// into later code, where the wait would also drain other loads in flight.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// A block's work list read 64 entries at a time, one entry per lane, so that
+// taking entry i is a lane read of a register, never a wait on memory: `first`
+// holds entries [0, 64), `cur` entries [base, base + 64) and `nxt` the 64 after
+// them. Valid indices are [0, 64) and [base, base + 128). advance(i), after
+// entry i has been used, moves the window at every multiple of 64 and fetches
+// the chunk 64 entries ahead of its first use; restart() goes back to entry 0
+// for another pass over the list. Entries are read through a buffer resource
+// of `count` entries, so indices past the end read 0 without a branch (a
+// branch around the load would make the compiler wait for it at the join).
+// Every lane of the wave calls each method with the same arguments.
+struct ListWindow {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int base, first, cur, nxt;
+  __device__ __forceinline__ int fetch(int i) const { return __builtin_amdgcn_raw_buffer_load_b32(rsrc, 4 * i, 0, 0); }
+  __device__ __forceinline__ void init(const int* l, int n, int lane) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<int*>(l), (short)0, 4 * n, 0x00020000);
+    base = 0;
+    first = cur = opaque(fetch(lane));
+    nxt = opaque(fetch(64 + lane));
+  }
+  __device__ __forceinline__ int get(int i) const {
+    // select values, not members: a select of member addresses becomes a memory read
+    const int f = first, c = cur, n = nxt;
+    const int v = i < 64 ? f : (i - base < 64 ? c : n);
+    return __builtin_amdgcn_readlane(v, i & 63);
+  }
+  // The refill is waited for before returning (one wait per 64 entries).
+  __device__ __forceinline__ void advance(int i, int lane) {
+    if (((i + 1) & 63) == 0) {
+      base += 64;
+      cur = nxt;
+      nxt = opaque(fetch(base + 64 + lane));
+    }
+  }
+  __device__ __forceinline__ void restart(int lane) {
+    if (base != 0) {
+      base = 0;
+      cur = first;
+      nxt = opaque(fetch(64 + lane));
+    }
+  }
+};
+
 __device__ __forceinline__ float swap_half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

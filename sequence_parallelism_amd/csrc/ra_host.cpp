@@ -14,6 +14,7 @@ constexpr int32_t kMaxHeads = 4096;
 
 // Tile shapes of the attention kernels (must match the device code).
 constexpr int kBf16BM = 128, kBf16BN = 64;
+constexpr int kBf16D128BM = 256;  // forward, bf16, head_dim 128
 constexpr int kF32BM = 64, kF32BN = 32;
 constexpr int kBwdBf16BK = 128, kBwdBf16BQ = 64;
 constexpr int kBwdF32BK = 64, kBwdF32BQ = 32;
@@ -101,11 +102,12 @@ int64_t local_len_bound(const ra_shape* shape, int32_t cp_size, int32_t n_docs) 
   return ((base + 2 * kDocBlock * nd + 2 + kDocBlock - 1) / kDocBlock) * kDocBlock;
 }
 
-Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition, int64_t s_local) {
+Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition, int64_t s_local,
+                   int bm) {
   Layout L{};
   L.s_local = (int)s_local;
   const bool bf16 = shape->in_dtype == RA_BF16;
-  L.bm = bf16 ? kBf16BM : kF32BM;
+  L.bm = bm > 0 ? bm : bf16 ? (shape->d == 128 ? kBf16D128BM : kBf16BM) : kF32BM;
   L.bn = bf16 ? kBf16BN : kF32BN;
   L.nqt = (L.s_local + L.bm - 1) / L.bm;
   L.nkt = (L.s_local + L.bn - 1) / L.bn;
@@ -127,8 +129,9 @@ Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, i
 BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition,
                      int64_t s_local) {
   BwdLayout B{};
-  B.fwd = attn_layout(shape, cp_size, n_docs_dev, partition, s_local);
   const bool bf16 = shape->in_dtype == RA_BF16;
+  // the dQ kernel walks the query-side work list in its own tile height
+  B.fwd = attn_layout(shape, cp_size, n_docs_dev, partition, s_local, bf16 ? kBf16BM : kF32BM);
   B.bk = bf16 ? kBwdBf16BK : kBwdF32BK;
   B.bq = bf16 ? kBwdBf16BQ : kBwdF32BQ;
   const int sl = B.fwd.s_local;

@@ -45,8 +45,10 @@ ra_status check_shape(const ra_shape* shape, int32_t cp_size, int32_t rank, int3
 ra_status check_cu(const int32_t* cu, int32_t n_docs, int64_t s_total);
 
 // Workspace layout of the attention entry points for a validated shape, given the
-// local length (local_len) and the partition.
-Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition, int64_t s_local);
+// local length (local_len) and the partition. The work list is built for query
+// tiles of bm rows; bm = 0 takes the forward kernel's tile height for the shape.
+Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition, int64_t s_local,
+                   int bm = 0);
 
 // Workspace layout of ra_backward for a validated shape.
 BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition,

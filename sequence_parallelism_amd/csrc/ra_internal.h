@@ -9,6 +9,7 @@ namespace ra {
 // Tile shapes of the attention kernels (query rows x keys per work-list entry).
 constexpr int kAttnBf16BM = 128;
 constexpr int kAttnBf16BN = 64;
+constexpr int kAttnBf16D128BM = 256;  // forward, bf16, head_dim 128 (two-group schedule)
 constexpr int kAttnF32BM = 64;
 constexpr int kAttnF32BN = 32;
 
@@ -25,6 +26,7 @@ struct AttnArgs;
 struct BwdArgs;
 
 hipError_t launch_ring_attn(const AttnArgs& a, int d, int in_bf16, int out_bf16, int steps, hipStream_t st);
+hipError_t launch_ring_attn_pp(const AttnArgs& a, int out_bf16, int steps, hipStream_t st);
 
 // Copies host cu_seqlens[0..n) into device memory dst (kernel arguments, no host staging buffer).
 hipError_t launch_upload_i32(const int32_t* host, int n, int32_t* dst, hipStream_t st);
