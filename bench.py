@@ -38,6 +38,9 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "causal-effective attention TFLOP/s per CP-rank share (% bf16 MFMA peak); permute GB/s"
+ATTN_KERNEL = "ring_attn_pp_kernel<true,false>"   # bf16 in and out, head_dim 128, fused steps
+# sources whose hash ties a committed counter profile to the kernel it measured
+KERNEL_SOURCES = ("ra_attn_pp.hip", "ra_common.h", "ra_device.h", "ra_internal.h")
 PART_CODE = {"contiguous": 0, "zigzag": 1, "striped": 2}
 
 
@@ -105,7 +108,7 @@ def traffic_from_profiles(kernel_src_sha):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("ra_attn.hip", "ra_common.h", "ra_device.h", "ra_internal.h"):
+    for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "sequence_parallelism_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
@@ -285,7 +288,7 @@ def main():
     traffic = traffic_from_profiles(src_sha)
     roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": "ring_attn_bf16_kernel<128,true,false>", "avg_launch_ms": attn["avg_ms"],
+                "kernel": ATTN_KERNEL, "avg_launch_ms": attn["avg_ms"],
                 "flops_per_launch": flops}
 
     cpu = None
