@@ -42,20 +42,17 @@ namespace ra {
 constexpr float kRescaleTau = 0.0f;
 
 // ---------------------------------------------------------------------------
-// bf16 inputs, MFMA path. 4 waves x 32 query rows, key tiles of 64.
+// bf16 inputs, MFMA path. 4 waves x 32 query rows, key tiles of 64. Launched
+// for head_dim 64 (head_dim 128 runs the two-group kernel of ra_attn_pp.hip).
 // ---------------------------------------------------------------------------
 template <int D, bool OUT_BF16, bool STEPS>
 __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a) {
   constexpr int BM = kAttnBf16BM, BN = kAttnBf16BN;
   static_assert(BM == 128 && BN == 64, "tile shape is baked into the lane mapping");
-  // LDS layout. head_dim 128: tiles arrive by direct global->LDS loads (no VGPR
-  // staging), rows of 256 B with 16-byte chunks XOR-swizzled against bank
-  // conflicts: K chunk c of row r at c ^ (r & 15) (16-byte reads down 16 rows),
-  // V chunk c of row r at c ^ 4 (r & 3) (transposing reads of 4 rows x 4 chunks).
-  // head_dim 64: register-staged tiles with padded rows.
-  constexpr bool DMA = D == 128;
-  constexpr int KROW = DMA ? D : D + 8;
-  constexpr int VROW = DMA ? D : D + 16;
+  // LDS: register-staged, double-buffered tiles with padded rows against bank
+  // conflicts (K pitch d + 8, V pitch d + 16 elements).
+  constexpr int KROW = D + 8;
+  constexpr int VROW = D + 16;
   constexpr int KTILE = BN * KROW, VTILE = BN * VROW, STAGE = KTILE + VTILE;
   constexpr int CHUNKS = BN * D / 8;         // 16-byte chunks per tile
   constexpr int PER = CHUNKS / 256;          // per thread
@@ -109,56 +106,26 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
     vslot[i] = r * VROW + c8 * 8;
   }
 
-  // Direct loads: wave w fills rows 16 w .. 16 w + 15 of a tile with 4 instructions
-  // of 4 rows each; lane L lands in chunk slot L % 16 of row L / 16 and fetches
-  // the global chunk that the swizzle maps there.
-  uint32_t dk_off[4], dv_off[4];
-  if constexpr (DMA) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * wave + 4 * i + (lane >> 4), pc = lane & 15;
-      dk_off[i] = (uint32_t)r * kv_row_bytes + ((uint32_t)g * D + 8 * (pc ^ (r & 15))) * 2u;
-      dv_off[i] = (uint32_t)r * kv_row_bytes + ((uint32_t)g * D + 8 * (pc ^ (4 * (r & 3)))) * 2u;
-    }
-  }
-
-  uint4 rk[DMA ? 1 : PER], rv[DMA ? 1 : PER];
+  uint4 rk[PER], rv[PER];
   auto load_tile = [&](int ent, int buf) {
     const int t = wl_step(ent), J = wl_tile(ent);
     const size_t cbase = (size_t)ring_owner(a.rank, t, a.cp) * chunk_bytes;
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc((const char*)a.k + cbase, chunk_bytes);
     const __amdgpu_buffer_rsrc_t vr = buffer_rsrc((const char*)a.v + cbase, chunk_bytes);
     const uint32_t toff = (uint32_t)J * BN * kv_row_bytes;
-    if constexpr (DMA) {
-      __attribute__((address_space(3))) char* kl =
-          (__attribute__((address_space(3))) char*)(smem + buf * STAGE) + 4096 * wave;
-      __attribute__((address_space(3))) char* vl = kl + KTILE * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16,
-                                                 (int)(toff + dk_off[i]), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16,
-                                                 (int)(toff + dv_off[i]), 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        rk[i] = buffer_load16(kr, toff + goff[i]);
-        rv[i] = buffer_load16(vr, toff + goff[i]);
-      }
+    for (int i = 0; i < PER; ++i) {
+      rk[i] = buffer_load16(kr, toff + goff[i]);
+      rv[i] = buffer_load16(vr, toff + goff[i]);
     }
   };
   auto store_tile = [&](int buf) {
-    if constexpr (DMA) {
-      __builtin_amdgcn_s_waitcnt(0);  // the direct loads have landed in LDS
-    } else {
-      __bf16* ks = smem + buf * STAGE;
-      __bf16* vs = ks + KTILE;
+    __bf16* ks = smem + buf * STAGE;
+    __bf16* vs = ks + KTILE;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        *(uint4*)(ks + kslot[i]) = rk[i];
-        *(uint4*)(vs + vslot[i]) = rv[i];
-      }
+    for (int i = 0; i < PER; ++i) {
+      *(uint4*)(ks + kslot[i]) = rk[i];
+      *(uint4*)(vs + vslot[i]) = rv[i];
     }
   };
   auto reset = [&]() {
@@ -233,7 +200,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           const int kr = kt * 32 + l32, kc = 2 * j + hi32;
-          const bf16x8 ka8 = *(const bf16x8*)(ks + kr * KROW + 8 * (DMA ? (kc ^ (kr & 15)) : kc));
+          const bf16x8 ka8 = *(const bf16x8*)(ks + kr * KROW + 8 * kc);
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka8, qreg[j], s[kt], 0, 0, 0);
         }
       __builtin_amdgcn_s_setprio(0);
@@ -287,8 +254,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int r0 = kt * 32 + jj * 16 + 4 * hi32 + ((lane & 15) >> 2);
-            int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            if constexpr (DMA) c0 ^= 32 * (r0 & 3);  // chunk ^= 4 (row & 3); rows r0 and r0 + 8 agree mod 4
+            const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
             const bf16x4 v0 = lds_read_tr(vs + r0 * VROW + c0);
             const bf16x4 v1 = lds_read_tr(vs + (r0 + 8) * VROW + c0);
             const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
