@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(256, 2) ring_attn_bf16_kernel(const AttnArgs a
     }
   };
 
-  ListWindow wl;
+  ListWindow<> wl;
   wl.init(list, n_ent, lane);
   int cur_t = 0;
   if (n_ent > 0) {
@@ -346,7 +346,7 @@ __global__ void __launch_bounds__(64) ring_attn_f32_kernel(const AttnArgs a) {
     }
   };
   int cur_t = 0;
-  ListWindow wl;
+  ListWindow<> wl;
   wl.init(list, n_ent, lane);
 
   for (int e = 0; e < n_ent; wl.advance(e, lane), ++e) {

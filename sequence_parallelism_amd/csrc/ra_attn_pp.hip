@@ -53,14 +53,6 @@ __device__ __forceinline__ void pp_wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// 16 bytes per lane from buffer r at byte offset voff into LDS: lane L writes
-// LDS bytes [lds + 16 L, lds + 16 L + 16). lds is wave-uniform. No register
-// results, so nothing is left for the compiler to wait on.
-__device__ __forceinline__ void pp_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
-}
-
 // Pins x in registers at this point of the program (an empty asm that reads
 // and rewrites it): the code computing x runs before later volatile asm, the
 // phase barrier included. Without it the optimiser sinks the softmax below the
@@ -121,7 +113,7 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
   const uint32_t kv_row_bytes = (uint32_t)a.hkv * D * 2u;
   const uint32_t chunk_bytes = (uint32_t)a.s_local * kv_row_bytes;
   const int n = clamp_count(a.wl_count[qt], a.wl_stride);
-  ListWindow wl;
+  ListWindow<> wl;
   wl.init(a.wl + (size_t)qt * a.wl_stride, n, lane);
 
   // Direct loads: wave wq of a group fills rows 16 wq .. 16 wq + 15 of a tile,
@@ -145,7 +137,7 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     const uint32_t toff = (uint32_t)wl_tile(ent) * BN * kv_row_bytes;
     const uint32_t base = lds_mine + (uint32_t)(idx % kPpStages) * (kPpTile * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pp_dma16(r, toff + d_off[i], base + 1024u * i);
+    for (int i = 0; i < 4; ++i) dma16_lds(r, toff + d_off[i], base + 1024u * i);
   };
 
   // Per-lane LDS element offsets inside a tile at key half kt = 0, j = 0 / jj = 0:

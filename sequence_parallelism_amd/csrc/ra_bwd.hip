@@ -170,12 +170,12 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
       __attribute__((address_space(3))) char* kl =
           (__attribute__((address_space(3))) char*)(smem + buf * STAGE) + 4096 * wave;
       __attribute__((address_space(3))) char* vl = kl + TILE * 2;
+      const uint32_t kb = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)kl);
+      const uint32_t vb = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)vl);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16,
-                                                 (int)(toff + d_off[i]), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16,
-                                                 (int)(toff + d_off[i]), 0, 0, 0);
+        dma16_lds(kr, toff + d_off[i], kb + 1024u * i);
+        dma16_lds(vr, toff + d_off[i], vb + 1024u * i);
       }
     } else {
 #pragma unroll
@@ -218,19 +218,19 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
     tr1_off[c] = (r0 + 8) * ROW + (DMA ? ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7)) : c0);
   }
 
-  ListWindow wl;
-  wl.init(list, n_ent, lane);
+  // The work list is read entry by entry here: a register window (as in the
+  // other kernels) costs this kernel spills at its 256-register limit.
   if (n_ent > 0) {
-    load_tile(wl.get(0), 0);
+    load_tile(list[0], 0);
     store_tile(0);
   }
   __syncthreads();
 
   for (int e = 0; e < n_ent; ++e) {
-    const int ent = wl.get(e);
+    const int ent = list[e];
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
     const bool ent_ok = t < a.cp && J < a.nkt && cls != CLS_SKIP;
-    if (e + 1 < n_ent) load_tile(wl.get(e + 1), (e + 1) & 1);
+    if (e + 1 < n_ent) load_tile(list[e + 1], (e + 1) & 1);
 
     const int ka = J * BN;
     const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
@@ -299,7 +299,6 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
 
     if (e + 1 < n_ent) store_tile((e + 1) & 1);
     __syncthreads();
-    wl.advance(e, lane);
   }
 
   if (row_ok) {
@@ -393,7 +392,11 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
     }
   }
   uint4 rq[DMA ? 1 : PER], ro[DMA ? 1 : PER];
-  float rl = INFINITY, rd = 0.f;  // wave 0: LSE * log2 e and D of row `lane` of the next tile
+  // wave 0: LSE and D of row `lane` of the next tile, as loaded; they are converted
+  // only when stored, so that no wait for these loads (which would also wait for
+  // the tile's direct loads issued before them) lands right after the issue
+  float rl = 0.f, rd = 0.f;
+  bool rok = false;
   auto load_tile = [&](int hh, int ent, int buf) {
     const int h = g * G + hh, I = wl_tile(ent);
     const uint32_t toff = (uint32_t)I * BQ * q_row_bytes + (uint32_t)h * D * 2u;
@@ -401,12 +404,12 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
       __attribute__((address_space(3))) char* ql =
           (__attribute__((address_space(3))) char*)(smem + buf * STAGE) + 4096 * wave;
       __attribute__((address_space(3))) char* ol = ql + TILE * 2;
+      const uint32_t qb = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)ql);
+      const uint32_t ob = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)ol);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (__attribute__((address_space(3))) void*)(ql + 1024 * i), 16,
-                                                 (int)(toff + d_off[i]), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (__attribute__((address_space(3))) void*)(ol + 1024 * i), 16,
-                                                 (int)(toff + d_off[i]), 0, 0, 0);
+        dma16_lds(qrs, toff + d_off[i], qb + 1024u * i);
+        dma16_lds(ors, toff + d_off[i], ob + 1024u * i);
       }
     } else {
 #pragma unroll
@@ -417,13 +420,10 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
     }
     if (wave == 0) {
       const int r = I * BQ + lane;
-      rl = INFINITY;
-      rd = 0.f;
-      if (r < a.s_local && I < a.nqt_kv) {
-        const float l = a.lse[(size_t)h * a.s_local + r];
-        rl = l == -INFINITY ? INFINITY : l * kLog2e;
-        rd = a.dsum[(size_t)h * a.s_local + r];
-      }
+      rok = r < a.s_local && I < a.nqt_kv;
+      const size_t idx = rok ? (size_t)h * a.s_local + r : 0;
+      rl = a.lse[idx];
+      rd = a.dsum[idx];
     }
   };
   auto store_tile = [&](int buf) {
@@ -439,8 +439,8 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
       }
     }
     if (wave == 0) {
-      rowv[buf][0][lane] = rl;
-      rowv[buf][1][lane] = rd;
+      rowv[buf][0][lane] = rok && rl != -INFINITY ? rl * kLog2e : INFINITY;  // LSE * log2 e; +inf: no row
+      rowv[buf][1][lane] = rok ? rd : 0.f;
     }
   };
 
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
     tr1_off[c] = (r0 + 8) * ROW + (DMA ? ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7)) : c0);
   }
 
-  ListWindow wl;
+  ListWindow<true> wl;
   wl.init(list, n_ent, lane);
   if (total > 0) {
     load_tile(0, wl.get(0), 0);

@@ -36,15 +36,17 @@ __device__ __forceinline__ int opaque(int x) {
 }
 
 // A block's work list read 64 entries at a time, one entry per lane, so that
-// taking entry i is a lane read of a register, never a wait on memory: `first`
-// holds entries [0, 64), `cur` entries [base, base + 64) and `nxt` the 64 after
-// them. Valid indices are [0, 64) and [base, base + 128). advance(i), after
-// entry i has been used, moves the window at every multiple of 64 and fetches
-// the chunk 64 entries ahead of its first use; restart() goes back to entry 0
-// for another pass over the list. Entries are read through a buffer resource
-// of `count` entries, so indices past the end read 0 without a branch (a
-// branch around the load would make the compiler wait for it at the join).
-// Every lane of the wave calls each method with the same arguments.
+// taking entry i is a lane read of a register, never a wait on memory: `cur`
+// holds entries [base, base + 64) and `nxt` the 64 after them; valid indices
+// are [base, base + 128). advance(i), after entry i has been used, moves the
+// window at every multiple of 64 and fetches the chunk 64 entries ahead of its
+// first use. With RESTART, `first` also keeps entries [0, 64) (valid at any
+// time) and restart() goes back to entry 0 for another pass over the list.
+// Entries are read through a buffer resource of `count` entries, so indices
+// past the end read 0 without a branch (a branch around the load would make
+// the compiler wait for it at the join). Every lane of the wave calls each
+// method with the same arguments.
+template <bool RESTART = false>
 struct ListWindow {
   __amdgpu_buffer_rsrc_t rsrc;
   int base, first, cur, nxt;
@@ -52,13 +54,18 @@ struct ListWindow {
   __device__ __forceinline__ void init(const int* l, int n, int lane) {
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<int*>(l), (short)0, 4 * n, 0x00020000);
     base = 0;
-    first = cur = opaque(fetch(lane));
+    cur = opaque(fetch(lane));
+    if constexpr (RESTART) first = cur;
     nxt = opaque(fetch(64 + lane));
   }
   __device__ __forceinline__ int get(int i) const {
     // select values, not members: a select of member addresses becomes a memory read
-    const int f = first, c = cur, n = nxt;
-    const int v = i < 64 ? f : (i - base < 64 ? c : n);
+    const int c = cur, n = nxt;
+    int v = i - base < 64 ? c : n;
+    if constexpr (RESTART) {
+      const int f = first;
+      v = i < 64 ? f : v;
+    }
     return __builtin_amdgcn_readlane(v, i & 63);
   }
   // The refill is waited for before returning (one wait per 64 entries).
@@ -70,6 +77,7 @@ struct ListWindow {
     }
   }
   __device__ __forceinline__ void restart(int lane) {
+    static_assert(RESTART, "restart needs the first chunk kept");
     if (base != 0) {
       base = 0;
       cur = first;
@@ -77,6 +85,17 @@ struct ListWindow {
     }
   }
 };
+
+// Direct global->LDS load of 16 bytes per lane from buffer r at byte offset
+// voff: lane L writes LDS bytes [lds + 16 L, lds + 16 L + 16); lds is
+// wave-uniform. Written in assembly so that the compiler does not track it:
+// otherwise it orders LDS reads after every direct load in flight (waiting for
+// the next tile's prefetch before the current tile's reads). The caller waits
+// for completion itself (s_waitcnt vmcnt) before publishing the data.
+__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ float swap_half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
