@@ -256,6 +256,14 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
           s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(ks + o), qreg[j], s[kt], 0, 0, 0);
           dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(vs + o), oreg[j], dp[kt], 0, 0, 0);
         }
+      // issue order: the LDS reads run 4 ahead of the MFMAs that use them
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 28; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       __builtin_amdgcn_s_setprio(0);
       // lane holds keys n = 32 kt + 8 (i/4) + 4 hi32 + (i%4) of its row; dS^T in place of S^T
       if (!need_mask) {
@@ -508,6 +516,14 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
           x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qh_q + rd_off[j]), kreg[j], x, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qh_o + rd_off[j]), vreg[j], dp, 0, 0, 0);
         }
+        // issue order: the LDS reads run 8 ahead of the MFMAs that use them
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         __builtin_amdgcn_s_setprio(0);
         // lane holds query rows n = 32 qh + 8 (i/4) + 4 hi32 + (i%4) of its key: P into x, dS into dp
         if (!need_mask) {
