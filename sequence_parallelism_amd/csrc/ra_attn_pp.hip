@@ -43,26 +43,6 @@ constexpr int kPpBN = kAttnBf16BN;      // 64 keys per tile
 constexpr int kPpStages = 3;
 constexpr int kPpTile = kPpBN * kPpD;  // elements of one K or V tile (16 KiB)
 
-// All 8 waves meet; the LDS reads issued before have returned (the direct
-// loads of the next phase may overwrite what they read).
-__device__ __forceinline__ void pp_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Waits until at most N of this wave's vector-memory operations are in flight.
-template <int N>
-__device__ __forceinline__ void pp_wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Pins x in registers at this point of the program (an empty asm that reads
-// and rewrites it): the code computing x runs before later volatile asm, the
-// phase barrier included. Without it the optimiser sinks the softmax below the
-// barrier that ends its phase, next to the products that consume P, and the
-// two groups' vector and matrix work no longer alternate.
-template <class T>
-__device__ __forceinline__ void pin(T& x) {
-  asm volatile("" : "+v"(x));
-}
-
 __device__ __forceinline__ bool entry_ok(int ent, const AttnArgs& a) {
   return wl_step(ent) < a.cp && wl_tile(ent) < a.nkt && wl_cls(ent) != CLS_SKIP;
 }
@@ -310,17 +290,17 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       issue(0, wl.get(0));
       if (n > 1) {
         issue(1, wl.get(1));
-        pp_wait_vm<4>();
+        wait_vmcnt<4>();
       } else {
-        pp_wait_vm<0>();
+        wait_vmcnt<0>();
       }
     } else {
       issue(0, wl.get(0));
     }
-    pp_barrier();
+    lds_barrier();
     if (grp == 1) {  // slot 0: group 1 has no phase yet; it loads V(1)
       if (n > 1) issue(1, wl.get(1));
-      pp_barrier();
+      lds_barrier();
     }
     for (int e = 0; e < n; ++e) {
       // M(e)
@@ -335,10 +315,10 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       }
       __builtin_amdgcn_s_setprio(0);
       if (grp == 1) {  // V(e) must have landed; V(e+1) may still be in flight
-        if (e + 1 < n) pp_wait_vm<4>();
-        else pp_wait_vm<0>();
+        if (e + 1 < n) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
       }
-      pp_barrier();
+      lds_barrier();
       // V(e)
       v_phase(e, sc);
       const bool more = e + 2 < n;
@@ -348,23 +328,26 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       wl.advance(e, lane);
       if (more) issue(e + 2, next_ent);
       if (grp == 0) {  // K(e+1) must have landed; K(e+2) may still be in flight
-        if (more) pp_wait_vm<4>();
-        else pp_wait_vm<0>();
+        if (more) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
       }
+      // pinned here, or the optimiser sinks the softmax below the barrier that ends
+      // its phase, next to the products that consume P, and the two groups' vector
+      // and matrix work no longer alternate
 #pragma unroll
       for (int k = 0; k < 4; ++k) pin(pb[k]);
 #pragma unroll
       for (int c = 0; c < NCT; ++c) pin(acc[c]);
       pin(l);
       pin(m);
-      pp_barrier();
+      lds_barrier();
     }
     // M(n): the last product
     __builtin_amdgcn_s_setprio(1);
     pv(n - 1);
     __builtin_amdgcn_s_setprio(0);
-    pp_barrier();
-    if (grp == 0) pp_barrier();  // last slot: group 1's M(n)
+    lds_barrier();
+    if (grp == 0) lds_barrier();  // last slot: group 1's M(n)
   }
 
   if constexpr (STEPS) {

@@ -97,6 +97,26 @@ __device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, uint32_t vof
                : "memory", "m0");
 }
 
+// Waits until at most N of this wave's vector-memory operations are in flight
+// (the count includes the direct loads above, which the compiler does not see).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier after this wave's LDS reads and writes have completed. It
+// does not wait for vector-memory loads (a __syncthreads fence would, draining
+// the direct loads kept in flight across barriers).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Pins x in registers at this point of the program (an empty asm that reads and
+// rewrites it): the code computing x runs before later volatile asm, a barrier
+// included, instead of being sunk past it towards x's uses.
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 __device__ __forceinline__ float swap_half_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
