@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
   const void* src_mine = grp ? a.v : a.k;
   // This group's tile of entry idx (list value ent) into stage idx % 3 (4 instructions).
   auto issue = [&](int idx, int ent) {
-    const size_t cbase = (size_t)ring_owner(a.rank, wl_step(ent), a.cp) * chunk_bytes;
+    const size_t cbase = (size_t)ring_owner_valid(a.rank, wl_step(ent), a.cp) * chunk_bytes;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc((const char*)src_mine + cbase, chunk_bytes);
     const uint32_t toff = (uint32_t)wl_tile(ent) * BN * kv_row_bytes;
     const uint32_t base = lds_mine + (uint32_t)(idx % kPpStages) * (kPpTile * 2u);
@@ -213,9 +213,29 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     __builtin_amdgcn_sched_group_barrier(kMfma, 6, 0);
   };
 
+  // What the mask of entry ent needs from memory, fetched one phase before its
+  // use: the key chunk's owner and, for per-document zigzag, the descriptor
+  // {first position, count} of the 64-slot block that is the key tile. The
+  // descriptor is a scalar load; the caller pins the three values before the
+  // barrier that ends the phase, so that their wait falls where the barrier
+  // waits anyway, not in the next softmax.
+  static_assert(kPpBN == kDocBlock, "a key tile is one doc-zigzag block");
+  const int n_blk = a.s_local / kDocBlock;
+  auto key_desc = [&](int ent, int& owner, int& dx, int& dy) {
+    owner = ring_owner_valid(a.rank, wl_step(ent), a.cp);
+    dx = 0;
+    dy = 0;
+    if (a.part == PART_DOC_ZIGZAG) {
+      const int2 d = blk_at(a.blk, entry_ok(ent, a) ? owner * n_blk + wl_tile(ent) : 0);
+      dx = d.x;
+      dy = d.y;
+    }
+  };
+
   // V phase: online softmax of S^T(e) into P^T(e). An entry that fails the range
-  // checks is a fully masked tile (P = 0, state unchanged).
-  auto v_phase = [&](int e, f32x16 (&sc)[2]) {
+  // checks is a fully masked tile (P = 0, state unchanged). owner, dx, dy: the
+  // entry's key_desc.
+  auto v_phase = [&](int e, f32x16 (&sc)[2], int owner, int dx, int dy) {
     const int ent = wl.get(e);
     const bool ok = entry_ok(ent, a);
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
@@ -229,23 +249,31 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     {
       const int ka = J * BN;
       const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
-      bool need_mask = !ok || kb - ka < BN || cls == CLS_PARTIAL;
-      TileMask tm{0, 0, 0, 0};
-      if (ok && need_mask) {
-        tm = tile_mask(pinfo, ring_owner(a.rank, t, a.cp), ka, kb, cls, row_ok, lo, hi);
-        need_mask = !__all(tile_all_visible(tm, BN) || !row_ok);
-      }
-      // lane holds keys n = 32 kt + 8 (i/4) + 4 hi32 + (i%4) of its row
-      if (need_mask) {
-        const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+      // The lane's row sees every key of the tile, none of them (the row is masked
+      // as a whole through the exponent's bias), or some (a per-key mask, taken
+      // when any lane of the wave needs it).
+      bool row_vis = ok;
+      if (ok && (kb - ka < BN || cls == CLS_PARTIAL)) {
+        Run k0{}, k1{};
+        if (a.part == PART_DOC_ZIGZAG) {  // the tile's keys: the first dy slots of the block
+          const int c = kb - ka < dy ? kb - ka : dy;
+          k0 = Run{dx, 1, c > 0 ? c : 0, 0};
+        } else {
+          runs_of(pinfo, owner, ka, kb, k0, k1);
+        }
+        const TileMask tm = tile_mask_runs(k0, k1, ka, kb, cls, row_ok, lo, hi);
+        const bool none = tm.la <= 0 && tm.lb <= 0;
+        row_vis = !none;
+        if (__any(!none && !tile_all_visible(tm, BN))) {
+          row_vis = true;
+          // after the shift, bit 32 kt + 8 (i/4) + (i%4) is the lane's element (kt, i)
+          const uint64_t vb = mask_bits(tm) >> (4 * hi32);
+          const uint32_t w[2] = {(uint32_t)vb, (uint32_t)(vb >> 32)};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int nk = kt * 32 + 8 * (i >> 2) + (i & 3);
-            const bool vis = ((unsigned)(nk + ba) < (unsigned)tm.la) | ((unsigned)(nk + bb) < (unsigned)tm.lb);
-            sc[kt][i] = vis ? sc[kt][i] : -INFINITY;
-          }
+            for (int i = 0; i < 16; ++i) sc[kt][i] = keep_or_ninf(sc[kt][i], w[kt], 8 * (i >> 2) + (i & 3));
+        }
       }
       // online softmax in the log2 domain; the running max is exact
       float mx = sc[0][0];
@@ -253,18 +281,22 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
-      mx = swap_half_max(mx) * C;
+      // a row that sees none of the tile: max -inf and P = exp2(-inf) = 0, through
+      // an added -inf (arithmetic rather than a select, which the compiler turns
+      // into a branch around the row maximum)
+      const float mb = row_vis ? 0.f : -INFINITY;
+      mx = __builtin_fmaf(swap_half_max(mx), C, mb);
       // rows that do not grow keep alpha = 1 exactly (their m may still be -inf)
       const bool grow = mx > m;
       const float alpha = grow ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
       m = grow ? mx : m;
-      const float m_use = m == -INFINITY ? 0.f : m;
+      const float bias = (m == -INFINITY ? 0.f : -m) + mb;
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][i], C, -m_use));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][i], C, bias));
           sc[kt][i] = p;
           rs += p;
         }
@@ -274,9 +306,8 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
         pb[2 * kt] = __builtin_convertvector(sc[kt].lo, bf16x8);
         pb[2 * kt + 1] = __builtin_convertvector(sc[kt].hi, bf16x8);
       }
-      // The accumulator is rescaled last: it is the destination of the products
-      // issued at the end of the previous phase, which may still be in the MFMA
-      // pipe behind the other wave's products when this phase starts.
+      // The compiler places the rescale right after alpha, ahead of the exps;
+      // holding it back until after them (an empty asm on rs) measured 4 % slower.
       if (__any(grow)) {
 #pragma unroll
         for (int c = 0; c < NCT; ++c) acc[c] *= alpha;
@@ -302,6 +333,8 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       if (n > 1) issue(1, wl.get(1));
       lds_barrier();
     }
+    int own_c, dx_c, dy_c;
+    key_desc(wl.get(0), own_c, dx_c, dy_c);
     for (int e = 0; e < n; ++e) {
       // M(e)
       f32x16 sc[2];
@@ -320,7 +353,9 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       }
       lds_barrier();
       // V(e)
-      v_phase(e, sc);
+      int own_n, dx_n, dy_n;
+      key_desc(wl.get(e + 1), own_n, dx_n, dy_n);  // entry n (past the end) reads as 0
+      v_phase(e, sc, own_c, dx_c, dy_c);
       const bool more = e + 2 < n;
       const int next_ent = more ? wl.get(e + 2) : 0;
       // a list refill (every 64 entries) is waited for here, which also waits for
@@ -340,7 +375,13 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       for (int c = 0; c < NCT; ++c) pin(acc[c]);
       pin(l);
       pin(m);
+      pin_s(own_n);
+      pin_s(dx_n);
+      pin_s(dy_n);
       lds_barrier();
+      own_c = own_n;
+      dx_c = dx_n;
+      dy_c = dy_n;
     }
     // M(n): the last product
     __builtin_amdgcn_s_setprio(1);

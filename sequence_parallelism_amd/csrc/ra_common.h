@@ -52,10 +52,20 @@ struct PartInfo {
   const int2* blk;  // doc-zigzag: [cp][s_local / 64] block descriptors {start, cnt}
 };
 
+// Doc-zigzag block descriptor i, read through the constant address space: at a
+// wave-uniform index this is a scalar load, waited for on the scalar/LDS
+// counter, so the wait does not also drain the vector-memory loads in flight
+// (the tile prefetch of the attention kernels). The table is never written
+// while a kernel reads it.
+__device__ __forceinline__ int2 blk_at(const int2* blk, int i) {
+  const __attribute__((address_space(4))) int* c = (const __attribute__((address_space(4))) int*)blk;
+  return make_int2(c[2 * i], c[2 * i + 1]);
+}
+
 // Global position of local index i of `owner` (-1: doc-zigzag padding).
 __device__ __forceinline__ int pos_of(const PartInfo& p, int owner, int i) {
   if (p.part == PART_DOC_ZIGZAG) {
-    const int2 b = p.blk[owner * (p.s_local / kDocBlock) + i / kDocBlock];
+    const int2 b = blk_at(p.blk, owner * (p.s_local / kDocBlock) + i / kDocBlock);
     const int o = i % kDocBlock;
     return o < b.y ? b.x + o : -1;
   }
@@ -76,12 +86,12 @@ __device__ __forceinline__ void runs_of(const PartInfo& p, int owner, int a, int
   if (p.part == PART_DOC_ZIGZAG) {  // [a, b) spans at most two blocks (aligned tiles of <= 128)
     const int nb = p.s_local / kDocBlock;
     const int A = a / kDocBlock, oa = a % kDocBlock, ea = (A + 1) * kDocBlock;
-    const int2 ba = p.blk[owner * nb + A];
+    const int2 ba = blk_at(p.blk, owner * nb + A);
     const int e0 = (b < ea ? b : ea) - A * kDocBlock;
     const int c0 = (e0 < ba.y ? e0 : ba.y) - oa;
     r0 = Run{ba.x + oa, 1, c0 > 0 ? c0 : 0, 0};
     if (b > ea) {
-      const int2 bb = p.blk[owner * nb + A + 1];
+      const int2 bb = blk_at(p.blk, owner * nb + A + 1);
       const int c1 = b - ea < bb.y ? b - ea : bb.y;
       r1 = Run{bb.x, 1, c1 > 0 ? c1 : 0, ea - a};
     }

@@ -140,6 +140,15 @@ __device__ __forceinline__ int head_of_slot(int hs, int hq) {
 // Chunk owner visited at ring step t (any t >= 0).
 __device__ __forceinline__ int ring_owner(int rank, int t, int cp) { return ((rank - t) % cp + cp) % cp; }
 
+// ring_owner without a division, for 0 <= rank < cp: exact for steps t < cp,
+// and `rank` for any other step (the step of an entry that fails its checks).
+__device__ __forceinline__ int ring_owner_valid(int rank, int t, int cp) {
+  return t < cp ? (rank >= t ? rank - t : rank - t + cp) : rank;
+}
+
+// Pins a wave-uniform value in scalar registers at this point (see pin()).
+__device__ __forceinline__ void pin_s(int& x) { asm volatile("" : "+s"(x)); }
+
 // Work-list length of a tile, clamped to the reserved stride.
 __device__ __forceinline__ int clamp_count(int n, int stride) { return n < 0 ? 0 : (n > stride ? stride : n); }
 
@@ -148,16 +157,16 @@ struct TileMask {
   int i0a, la, i0b, lb;
 };
 
-__device__ __forceinline__ TileMask tile_mask(const PartInfo& p, int owner, int ka, int kb, int cls, bool row_ok,
-                                              int lo, int hi) {
+// The mask of a lane whose row sees positions [lo, hi], for the tile's keys
+// [ka, kb) given as the runs k0, k1 (runs_of).
+__device__ __forceinline__ TileMask tile_mask_runs(const Run& k0, const Run& k1, int ka, int kb, int cls, bool row_ok,
+                                                   int lo, int hi) {
   TileMask t{0, 0, 0, 0};
   if (!row_ok) return t;
   if (cls == CLS_FULL) {
     t.la = kb - ka;
     return t;
   }
-  Run k0, k1;
-  runs_of(p, owner, ka, kb, k0, k1);
   int n0, n1;
   run_range(k0, lo, hi, n0, n1);  // an empty slot gives an empty interval
   t.i0a = k0.off + n0;
@@ -166,6 +175,32 @@ __device__ __forceinline__ TileMask tile_mask(const PartInfo& p, int owner, int 
   t.i0b = k1.off + n0;
   t.lb = n1 >= n0 ? n1 - n0 + 1 : 0;
   return t;
+}
+
+__device__ __forceinline__ TileMask tile_mask(const PartInfo& p, int owner, int ka, int kb, int cls, bool row_ok,
+                                              int lo, int hi) {
+  if (!row_ok || cls == CLS_FULL) return tile_mask_runs(Run{}, Run{}, ka, kb, cls, row_ok, lo, hi);
+  Run k0, k1;
+  runs_of(p, owner, ka, kb, k0, k1);
+  return tile_mask_runs(k0, k1, ka, kb, cls, row_ok, lo, hi);
+}
+
+// The lane's interval set as a bit mask over the tile's indices: bit n set when
+// index n is visible (tiles of at most 64 indices).
+__device__ __forceinline__ uint64_t interval_bits(int i0, int len) {
+  if (len <= 0) return 0;
+  const uint64_t m = len >= 64 ? ~0ull : (1ull << len) - 1ull;
+  return m << (i0 & 63);  // a non-empty interval has i0 + len <= 64
+}
+__device__ __forceinline__ uint64_t mask_bits(const TileMask& t) {
+  return interval_bits(t.i0a, t.la) | interval_bits(t.i0b, t.lb);
+}
+
+// x when bit b of w is set, else -inf; branch-free (a sign-extending bit field
+// extract and one bitwise select), for the per-element masks of score tiles.
+__device__ __forceinline__ float keep_or_ninf(float x, uint32_t w, int b) {
+  const int mk = (int)(w << (31 - b)) >> 31;  // all ones when the bit is set
+  return __int_as_float((__float_as_int(x) & mk) | (~mk & (int)0xff800000u));
 }
 
 // True when the lane's interval set covers all n indices of the tile.
