@@ -43,9 +43,17 @@ constexpr int kPpBN = kAttnBf16BN;      // 64 keys per tile
 constexpr int kPpStages = 3;
 constexpr int kPpTile = kPpBN * kPpD;  // elements of one K or V tile (16 KiB)
 
-__device__ __forceinline__ bool entry_ok(int ent, const AttnArgs& a) {
-  return wl_step(ent) < a.cp && wl_tile(ent) < a.nkt && wl_cls(ent) != CLS_SKIP;
-}
+// List entries as this kernel reads them: an entry that fails the range checks
+// becomes 0 (class SKIP: a fully masked tile), and the ragged last key tile, if
+// any, is PARTIAL. After this, the class alone decides how a tile is masked.
+struct PpCook {
+  int cp, nkt, ragged;  // ragged: the key tile shorter than 64 keys, or -1
+  __device__ __forceinline__ int operator()(int v) const {
+    const int t = wl_step(v), J = wl_tile(v), c = wl_cls(v);
+    const bool ok = t < cp && J < nkt && c != CLS_SKIP;
+    return ok ? wl_pack(t, J, J == ragged ? CLS_PARTIAL : c) : 0;
+  }
+};
 
 }  // namespace
 
@@ -93,31 +101,69 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
   const uint32_t kv_row_bytes = (uint32_t)a.hkv * D * 2u;
   const uint32_t chunk_bytes = (uint32_t)a.s_local * kv_row_bytes;
   const int n = clamp_count(a.wl_count[qt], a.wl_stride);
-  ListWindow<> wl;
-  wl.init(a.wl + (size_t)qt * a.wl_stride, n, lane);
+  ListWindow<false, PpCook> wl;
+  wl.init(a.wl + (size_t)qt * a.wl_stride, n, lane, PpCook{a.cp, a.nkt, a.s_local % BN ? a.nkt - 1 : -1});
 
   // Direct loads: wave wq of a group fills rows 16 wq .. 16 wq + 15 of a tile,
   // 4 rows per instruction; lane L lands in chunk slot L % 16 of row L / 16 and
   // fetches the chunk that the swizzle maps there (group 0: K, group 1: V).
+  // d_off[i] is that offset within the tile less 1024 i, the immediate offset
+  // of load i (dma16x4_lds).
   uint32_t d_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * wq + 4 * i + (lane >> 4), pc = lane & 15;
     const int chunk = grp ? (pc ^ (4 * (r & 3))) : (pc ^ (r & 15));
-    d_off[i] = (uint32_t)r * kv_row_bytes + ((uint32_t)g * D + 8 * chunk) * 2u;
+    d_off[i] = (uint32_t)r * kv_row_bytes + ((uint32_t)g * D + 8 * chunk) * 2u - 1024u * i;
   }
   const uint32_t lds_k = (uint32_t)(size_t)(__attribute__((address_space(3))) __bf16*)&kbuf[0][0];
   const uint32_t lds_v = (uint32_t)(size_t)(__attribute__((address_space(3))) __bf16*)&vbuf[0][0];
   const uint32_t lds_mine = (grp ? lds_v : lds_k) + 4096u * wq;
   const void* src_mine = grp ? a.v : a.k;
-  // This group's tile of entry idx (list value ent) into stage idx % 3 (4 instructions).
-  auto issue = [&](int idx, int ent) {
-    const size_t cbase = (size_t)ring_owner_valid(a.rank, wl_step(ent), a.cp) * chunk_bytes;
+
+  // The work list is consumed through a pipeline: each entry is fetched and
+  // decoded once, in the V phase two entries before its own, where its tiles are
+  // loaded. The record keeps the list value, the owner of the key chunk and,
+  // under per-document zigzag, the descriptor {first position, count} of the
+  // 64-slot block that is the key tile (a scalar load; the record is pinned
+  // before the barrier that ends the phase, so the wait falls where the barrier
+  // waits anyway). Indices past the end read as 0: an entry that fails the range
+  // checks (as do those that fail them), whose loads (tile 0 of a valid chunk)
+  // land in a stage nothing reads.
+  struct Ent {
+    int ent, owner, dx, dy;
+  };
+  static_assert(kPpBN == kDocBlock, "a key tile is one doc-zigzag block");
+  const int n_blk = a.s_local / kDocBlock;
+  auto fetch = [&](int idx) {
+    Ent x;
+    x.ent = wl.get(idx);
+    const int t = wl_step(x.ent);  // below cp
+    x.owner = a.rank - t + (a.rank < t ? a.cp : 0);
+    x.dx = 0;
+    x.dy = 0;
+    if (a.part == PART_DOC_ZIGZAG) {
+      const int2 d = blk_at(a.blk, x.owner * n_blk + wl_tile(x.ent));
+      x.dx = d.x;
+      x.dy = d.y;
+    }
+    return x;
+  };
+  auto pin_ent = [](Ent& x) {
+    pin_s(x.ent);
+    pin_s(x.owner);
+    pin_s(x.dx);
+    pin_s(x.dy);
+  };
+  // This group's tile of entry x into LDS stage st (4 direct loads per wave).
+  auto issue = [&](int st, const Ent& x) {
+    const size_t cbase = (size_t)x.owner * chunk_bytes;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc((const char*)src_mine + cbase, chunk_bytes);
-    const uint32_t toff = (uint32_t)wl_tile(ent) * BN * kv_row_bytes;
-    const uint32_t base = lds_mine + (uint32_t)(idx % kPpStages) * (kPpTile * 2u);
+    const uint32_t toff = (uint32_t)wl_tile(x.ent) * BN * kv_row_bytes;
+    uint32_t voff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16_lds(r, toff + d_off[i], base + 1024u * i);
+    for (int i = 0; i < 4; ++i) voff[i] = toff + d_off[i];
+    dma16x4_lds(r, voff, lds_mine + (uint32_t)st * (kPpTile * 2u));
   };
 
   // Per-lane LDS element offsets inside a tile at key half kt = 0, j = 0 / jj = 0:
@@ -136,9 +182,10 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     }
   }
 
-  // M phase parts: S^T(e) = K(e) Q^T into sc, and O^T += V(e-1)^T P^T(e-1).
-  auto qk = [&](int e, f32x16 (&sc)[2]) {
-    const __bf16* ks = kbuf[e % kPpStages];
+  // M phase parts: S^T(e) = K(e) Q^T into sc from stage st, and
+  // O^T += V(e-1)^T P^T(e-1) from stage st.
+  auto qk = [&](int st, f32x16 (&sc)[2]) {
+    const __bf16* ks = kbuf[st];
     int ko[NKD];
 #pragma unroll
     for (int j = 0; j < NKD; ++j) ko[j] = opaque(k_off[j]);
@@ -150,8 +197,8 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
         sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka8, qreg[j], j ? sc[kt] : f32x16{}, 0, 0, 0);
       }
   };
-  auto pv = [&](int e) {
-    const __bf16* vs = vbuf[e % kPpStages];
+  auto pv = [&](int st) {
+    const __bf16* vs = vbuf[st];
     int vo[NCT];
 #pragma unroll
     for (int c = 0; c < NCT; ++c) vo[c] = opaque(v_off[c]);
@@ -213,31 +260,12 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     __builtin_amdgcn_sched_group_barrier(kMfma, 6, 0);
   };
 
-  // What the mask of entry ent needs from memory, fetched one phase before its
-  // use: the key chunk's owner and, for per-document zigzag, the descriptor
-  // {first position, count} of the 64-slot block that is the key tile. The
-  // descriptor is a scalar load; the caller pins the three values before the
-  // barrier that ends the phase, so that their wait falls where the barrier
-  // waits anyway, not in the next softmax.
-  static_assert(kPpBN == kDocBlock, "a key tile is one doc-zigzag block");
-  const int n_blk = a.s_local / kDocBlock;
-  auto key_desc = [&](int ent, int& owner, int& dx, int& dy) {
-    owner = ring_owner_valid(a.rank, wl_step(ent), a.cp);
-    dx = 0;
-    dy = 0;
-    if (a.part == PART_DOC_ZIGZAG) {
-      const int2 d = blk_at(a.blk, entry_ok(ent, a) ? owner * n_blk + wl_tile(ent) : 0);
-      dx = d.x;
-      dy = d.y;
-    }
-  };
-
-  // V phase: online softmax of S^T(e) into P^T(e). An entry that fails the range
-  // checks is a fully masked tile (P = 0, state unchanged). owner, dx, dy: the
-  // entry's key_desc.
-  auto v_phase = [&](int e, f32x16 (&sc)[2], int owner, int dx, int dy) {
-    const int ent = wl.get(e);
-    const bool ok = entry_ok(ent, a);
+  // V phase: online softmax of S^T(e) into P^T(e) for the entry record x. An
+  // entry that fails the range checks is a fully masked tile (P = 0, state
+  // unchanged).
+  auto v_phase = [&](f32x16 (&sc)[2], const Ent& x) {
+    const int ent = x.ent, owner = x.owner, dx = x.dx, dy = x.dy;
+    const bool ok = wl_cls(ent) != CLS_SKIP;
     const int t = wl_step(ent), J = wl_tile(ent), cls = wl_cls(ent);
     if constexpr (STEPS) {
       while (ok && cur_t < t) {
@@ -247,13 +275,13 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       }
     }
     {
-      const int ka = J * BN;
-      const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
       // The lane's row sees every key of the tile, none of them (the row is masked
       // as a whole through the exponent's bias), or some (a per-key mask, taken
       // when any lane of the wave needs it).
       bool row_vis = ok;
-      if (ok && (kb - ka < BN || cls == CLS_PARTIAL)) {
+      if (cls == CLS_PARTIAL) {  // the ragged key tile included
+        const int ka = J * BN;
+        const int kb = ka + BN < a.s_local ? ka + BN : a.s_local;
         Run k0{}, k1{};
         if (a.part == PART_DOC_ZIGZAG) {  // the tile's keys: the first dy slots of the block
           const int c = kb - ka < dy ? kb - ka : dy;
@@ -317,55 +345,42 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
 
   if (n > 0) {
     // prologue: group 0 loads K(0), K(1) and publishes K(0); group 1 loads V(0)
+    // (entry 1 is loaded even when n == 1: past the end it reads as entry 0)
+    Ent x0 = fetch(0), x1 = fetch(1);
+    issue(0, x0);
     if (grp == 0) {
-      issue(0, wl.get(0));
-      if (n > 1) {
-        issue(1, wl.get(1));
-        wait_vmcnt<4>();
-      } else {
-        wait_vmcnt<0>();
-      }
-    } else {
-      issue(0, wl.get(0));
+      issue(1, x1);
+      wait_vmcnt<4>();
     }
     lds_barrier();
     if (grp == 1) {  // slot 0: group 1 has no phase yet; it loads V(1)
-      if (n > 1) issue(1, wl.get(1));
+      issue(1, x1);
       lds_barrier();
     }
-    int own_c, dx_c, dy_c;
-    key_desc(wl.get(0), own_c, dx_c, dy_c);
+    int st = 0;  // stage of entry e; stage of e - 1 and of e + 2: (st + 2) % 3
     for (int e = 0; e < n; ++e) {
+      const int st_b = st == 0 ? 2 : st - 1;
       // M(e)
       f32x16 sc[2];
       __builtin_amdgcn_s_setprio(1);
       if (e > 0) {
-        qk(e, sc);
-        pv(e - 1);
+        qk(st, sc);
+        pv(st_b);
         m_order();
       } else {
-        qk(e, sc);
+        qk(st, sc);
       }
       __builtin_amdgcn_s_setprio(0);
-      if (grp == 1) {  // V(e) must have landed; V(e+1) may still be in flight
-        if (e + 1 < n) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
-      }
+      if (grp == 1) wait_vmcnt<4>();  // V(e) must have landed; V(e+1) may still be in flight
       lds_barrier();
       // V(e)
-      int own_n, dx_n, dy_n;
-      key_desc(wl.get(e + 1), own_n, dx_n, dy_n);  // entry n (past the end) reads as 0
-      v_phase(e, sc, own_c, dx_c, dy_c);
-      const bool more = e + 2 < n;
-      const int next_ent = more ? wl.get(e + 2) : 0;
+      Ent x2 = fetch(e + 2);
+      v_phase(sc, x0);
       // a list refill (every 64 entries) is waited for here, which also waits for
       // this wave's tile loads in flight: group 0 needs K(e+1) now anyway
       wl.advance(e, lane);
-      if (more) issue(e + 2, next_ent);
-      if (grp == 0) {  // K(e+1) must have landed; K(e+2) may still be in flight
-        if (more) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
-      }
+      issue(st_b, x2);
+      if (grp == 0) wait_vmcnt<4>();  // K(e+1) must have landed; K(e+2) may still be in flight
       // pinned here, or the optimiser sinks the softmax below the barrier that ends
       // its phase, next to the products that consume P, and the two groups' vector
       // and matrix work no longer alternate
@@ -375,18 +390,17 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       for (int c = 0; c < NCT; ++c) pin(acc[c]);
       pin(l);
       pin(m);
-      pin_s(own_n);
-      pin_s(dx_n);
-      pin_s(dy_n);
+      pin_ent(x2);
       lds_barrier();
-      own_c = own_n;
-      dx_c = dx_n;
-      dy_c = dy_n;
+      x0 = x1;
+      x1 = x2;
+      st = st == 2 ? 0 : st + 1;
     }
     // M(n): the last product
     __builtin_amdgcn_s_setprio(1);
-    pv(n - 1);
+    pv(st == 0 ? 2 : st - 1);
     __builtin_amdgcn_s_setprio(0);
+    wait_vmcnt<0>();  // the two loads past the end must land before the workgroup's LDS is released
     lds_barrier();
     if (grp == 0) lds_barrier();  // last slot: group 1's M(n)
   }

@@ -45,18 +45,26 @@ __device__ __forceinline__ int opaque(int x) {
 // Entries are read through a buffer resource of `count` entries, so indices
 // past the end read 0 without a branch (a branch around the load would make
 // the compiler wait for it at the join). Every lane of the wave calls each
-// method with the same arguments.
-template <bool RESTART = false>
+// method with the same arguments. An optional `cook` maps each entry once, as
+// it is loaded (one lane per entry), to the value that get() returns.
+struct NoCook {
+  __device__ __forceinline__ int operator()(int v) const { return v; }
+};
+template <bool RESTART = false, class Cook = NoCook>
 struct ListWindow {
   __amdgpu_buffer_rsrc_t rsrc;
   int base, first, cur, nxt;
-  __device__ __forceinline__ int fetch(int i) const { return __builtin_amdgcn_raw_buffer_load_b32(rsrc, 4 * i, 0, 0); }
-  __device__ __forceinline__ void init(const int* l, int n, int lane) {
+  Cook cook;
+  __device__ __forceinline__ int fetch(int i) const {
+    return cook(opaque(__builtin_amdgcn_raw_buffer_load_b32(rsrc, 4 * i, 0, 0)));
+  }
+  __device__ __forceinline__ void init(const int* l, int n, int lane, Cook c = Cook{}) {
+    cook = c;
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<int*>(l), (short)0, 4 * n, 0x00020000);
     base = 0;
-    cur = opaque(fetch(lane));
+    cur = fetch(lane);
     if constexpr (RESTART) first = cur;
-    nxt = opaque(fetch(64 + lane));
+    nxt = fetch(64 + lane);
   }
   __device__ __forceinline__ int get(int i) const {
     // select values, not members: a select of member addresses becomes a memory read
@@ -73,7 +81,7 @@ struct ListWindow {
     if (((i + 1) & 63) == 0) {
       base += 64;
       cur = nxt;
-      nxt = opaque(fetch(base + 64 + lane));
+      nxt = fetch(base + 64 + lane);
     }
   }
   __device__ __forceinline__ void restart(int lane) {
@@ -81,7 +89,7 @@ struct ListWindow {
     if (base != 0) {
       base = 0;
       cur = first;
-      nxt = opaque(fetch(64 + lane));
+      nxt = fetch(64 + lane);
     }
   }
 };
@@ -91,10 +99,30 @@ struct ListWindow {
 // wave-uniform. Written in assembly so that the compiler does not track it:
 // otherwise it orders LDS reads after every direct load in flight (waiting for
 // the next tile's prefetch before the current tile's reads). The caller waits
-// for completion itself (s_waitcnt vmcnt) before publishing the data.
+// for completion itself (s_waitcnt vmcnt) before publishing the data. A direct
+// load that reads M0 needs one wait state after a scalar write of M0 (the
+// compiler's hazard pass cannot see into the asm, hence the s_nop).
 __device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(r)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(r)
                : "memory", "m0");
+}
+
+// Four direct loads of 16 bytes per lane, as dma16_lds at (voff[i] + 1024 i,
+// lds + 1024 i) for i = 0..3. The immediate offset applies to both the buffer
+// and the LDS address, so one M0 serves all four (voff[i] carries the rest).
+// lds is wave-uniform; the read of lane 0 keeps it in a scalar register where
+// the compiler cannot prove that.
+__device__ __forceinline__ void dma16x4_lds(__amdgpu_buffer_rsrc_t r, const uint32_t (&voff)[4], uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+      "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(r)
+      : "memory", "m0");
 }
 
 // Waits until at most N of this wave's vector-memory operations are in flight
