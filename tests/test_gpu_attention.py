@@ -95,6 +95,18 @@ def test_ragged_tiles_and_noncausal(part):
         _check_rank(g, cp, rank, part, causal=False)
 
 
+@pytest.mark.parametrize("S,cp,part", [(16, 1, "contiguous"), (64, 1, "contiguous"), (100, 1, "contiguous"),
+                                       (128, 2, "zigzag"), (200, 2, "striped"), (384, 3, "zigzag")])
+def test_short_work_lists(S, cp, part):
+    """Query tiles whose work lists hold one or two entries (the head_dim-128 kernel
+    still loads tiles two entries ahead, past the end of the list) and ragged key
+    tiles, causal and not."""
+    g = _case_inputs(S, 2, 1, 128, "bf16", seed=S + cp)
+    for rank in range(cp):
+        _check_rank(g, cp, rank, part, causal=True)
+        _check_rank(g, cp, rank, part, causal=False)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("out_bf16", [False, True])
 def test_head_dims_and_output_dtypes(d, out_bf16):
