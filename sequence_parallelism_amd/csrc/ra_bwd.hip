@@ -302,6 +302,14 @@ __global__ void __launch_bounds__(256, 2) ring_bwd_dq_bf16_kernel(const BwdArgs 
             acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, jj ? sb1 : sb0, acc[c], 0, 0, 0);
           }
       }
+      // issue order: the transposing reads run 2 MFMAs ahead of their use
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 14; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_s_setprio(0);
     }
 
@@ -573,6 +581,15 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
             dv[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, jj ? pb1 : pb0, dv[c], 0, 0, 0);
             dk[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt8, jj ? sb1 : sb0, dk[c], 0, 0, 0);
           }
+        // issue order: the transposing reads run 4 MFMAs ahead of their use (left
+        // to itself the compiler waits for each group of 8 before its 4 MFMAs)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_s_setprio(0);
       }
     }
