@@ -518,28 +518,38 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
         const __bf16* qh_q = qs + qh * 32 * ROW;
         const __bf16* qh_o = os + qh * 32 * ROW;
         f32x16 x = f32x16{}, dp = f32x16{};
+        // this half's LSE and D (lane rows 8 i4 + 4 hi32 + 0..3), read under the products
+        f32x4 Lr[4], Dr[4];
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < NKD; ++j) {
           x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qh_q + rd_off[j]), kreg[j], x, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qh_o + rd_off[j]), vreg[j], dp, 0, 0, 0);
         }
-        // issue order: the LDS reads run 8 ahead of the MFMAs that use them
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          Lr[i4] = *(const f32x4*)(l2s + qh * 32 + 8 * i4 + 4 * hi32);
+          Dr[i4] = *(const f32x4*)(dss + qh * 32 + 8 * i4 + 4 * hi32);
+        }
+        // issue order: the LDS reads run 8 ahead of the MFMAs that use them; the
+        // 8 row-vector reads go under the last products
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
         __builtin_amdgcn_s_setprio(0);
         // lane holds query rows n = 32 qh + 8 (i/4) + 4 hi32 + (i%4) of its key: P into x, dS into dp
         if (!need_mask) {
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
-            const int n0 = qh * 32 + 8 * i4 + 4 * hi32;
-            const f32x4 L = *(const f32x4*)(l2s + n0);
-            const f32x4 Dd = *(const f32x4*)(dss + n0);
+            const f32x4 L = Lr[i4], Dd = Dr[i4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int i = 4 * i4 + u;
@@ -552,9 +562,7 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
           const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
-            const int n0 = qh * 32 + 8 * i4 + 4 * hi32;
-            const f32x4 L = *(const f32x4*)(l2s + n0);
-            const f32x4 Dd = *(const f32x4*)(dss + n0);
+            const f32x4 L = Lr[i4], Dd = Dr[i4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int i = 4 * i4 + u, n = qh * 32 + 8 * i4 + u;
