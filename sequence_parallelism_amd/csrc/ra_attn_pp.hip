@@ -118,7 +118,8 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
   }
   const uint32_t lds_k = (uint32_t)(size_t)(__attribute__((address_space(3))) __bf16*)&kbuf[0][0];
   const uint32_t lds_v = (uint32_t)(size_t)(__attribute__((address_space(3))) __bf16*)&vbuf[0][0];
-  const uint32_t lds_mine = (grp ? lds_v : lds_k) + 4096u * wq;
+  // wave-uniform; read from lane 0 so that it stays in a scalar register
+  const uint32_t lds_mine = __builtin_amdgcn_readfirstlane((grp ? lds_v : lds_k) + 4096u * wq);
   const void* src_mine = grp ? a.v : a.k;
 
   // The work list is consumed through a pipeline: each entry is fetched and
@@ -157,7 +158,7 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
   };
   // This group's tile of entry x into LDS stage st (4 direct loads per wave).
   auto issue = [&](int st, const Ent& x) {
-    const size_t cbase = (size_t)x.owner * chunk_bytes;
+    const size_t cbase = (size_t)(uint32_t)x.owner * chunk_bytes;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc((const char*)src_mine + cbase, chunk_bytes);
     const uint32_t toff = (uint32_t)wl_tile(x.ent) * BN * kv_row_bytes;
     uint32_t voff[4];
