@@ -156,15 +156,16 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     pin_s(x.dx);
     pin_s(x.dy);
   };
-  // This group's tile of entry x into LDS stage st (4 direct loads per wave).
-  auto issue = [&](int st, const Ent& x) {
+  // Stages are passed as byte offsets (stage * 16 KiB), held in scalar registers.
+  // This group's tile of entry x into the LDS stage at offset sb (4 direct loads per wave).
+  auto issue = [&](uint32_t sb, const Ent& x) {
     const size_t cbase = (size_t)(uint32_t)x.owner * chunk_bytes;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc((const char*)src_mine + cbase, chunk_bytes);
     const uint32_t toff = (uint32_t)wl_tile(x.ent) * BN * kv_row_bytes;
     uint32_t voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) voff[i] = toff + d_off[i];
-    dma16x4_lds(r, voff, lds_mine + (uint32_t)st * (kPpTile * 2u));
+    dma16x4_lds(r, voff, lds_mine + sb);
   };
 
   // Per-lane LDS element offsets inside a tile at key half kt = 0, j = 0 / jj = 0:
@@ -183,34 +184,44 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     }
   }
 
-  // M phase parts: S^T(e) = K(e) Q^T into sc from stage st, and
-  // O^T += V(e-1)^T P^T(e-1) from stage st.
-  auto qk = [&](int st, f32x16 (&sc)[2]) {
-    const __bf16* ks = kbuf[st];
-    int ko[NKD];
+  // M phase parts: S^T(e) = K(e) Q^T into sc from the stage at sb, and
+  // O^T += V(e-1)^T P^T(e-1) from the stage at sb.
+  typedef __attribute__((address_space(3))) char lds_char;
+  // The same offsets as LDS byte addresses in stage 0: a read's address is then one
+  // add of the stage's scalar offset. The per-step kernel, whose flushes need more
+  // registers, re-derives them from the element offsets at each use instead (kept
+  // opaque to the optimiser, which otherwise hoists them into registers of their own).
+  uint32_t k_adr[NKD], v_adr[NCT];
 #pragma unroll
-    for (int j = 0; j < NKD; ++j) ko[j] = opaque(k_off[j]);
+  for (int j = 0; j < NKD; ++j) k_adr[j] = lds_k + 2u * (uint32_t)k_off[j];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) v_adr[c] = lds_v + 2u * (uint32_t)v_off[c];
+  auto qk = [&](uint32_t sb, f32x16 (&sc)[2]) {
+    uint32_t ko[NKD];
+#pragma unroll
+    for (int j = 0; j < NKD; ++j) ko[j] = (STEPS ? lds_k + 2u * (uint32_t)opaque(k_off[j]) : k_adr[j]) + sb;
 #pragma unroll
     for (int j = 0; j < NKD; ++j)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 ka8 = *(const bf16x8*)(ks + ko[j] + kt * 32 * D);
+        const bf16x8 ka8 = *(const __attribute__((address_space(3))) bf16x8*)((const lds_char*)(size_t)ko[j] + kt * 32 * D * 2);
         sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka8, qreg[j], j ? sc[kt] : f32x16{}, 0, 0, 0);
       }
   };
-  auto pv = [&](int st) {
-    const __bf16* vs = vbuf[st];
-    int vo[NCT];
+  auto pv = [&](uint32_t sb) {
+    uint32_t vo[NCT];
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) vo[c] = opaque(v_off[c]);
+    for (int c = 0; c < NCT; ++c) vo[c] = (STEPS ? lds_v + 2u * (uint32_t)opaque(v_off[c]) : v_adr[c]) + sb;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const __bf16* p = vs + vo[c] + (kt * 32 + jj * 16) * D;
-          const bf16x8 va = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 8 * D), 0, 1, 2, 3, 4, 5, 6, 7);
+          const lds_char* p = (const lds_char*)(size_t)vo[c] + (kt * 32 + jj * 16) * D * 2;
+          const bf16x8 va = __builtin_shufflevector(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p),
+                                                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * D)),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
           acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[2 * kt + jj], acc[c], 0, 0, 0);
         }
   };
@@ -350,26 +361,27 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     Ent x0 = fetch(0), x1 = fetch(1);
     issue(0, x0);
     if (grp == 0) {
-      issue(1, x1);
+      issue(kPpTile * 2u, x1);
       wait_vmcnt<4>();
     }
     lds_barrier();
     if (grp == 1) {  // slot 0: group 1 has no phase yet; it loads V(1)
-      issue(1, x1);
+      issue(kPpTile * 2u, x1);
       lds_barrier();
     }
-    int st = 0;  // stage of entry e; stage of e - 1 and of e + 2: (st + 2) % 3
+    // byte offsets of the stages of entry e (s_cur), of e - 1 and e + 2 (s_prv),
+    // and of e + 1 (s_nxt); they rotate by one stage per entry
+    uint32_t s_cur = 0, s_nxt = kPpTile * 2u, s_prv = 2 * kPpTile * 2u;
     for (int e = 0; e < n; ++e) {
-      const int st_b = st == 0 ? 2 : st - 1;
       // M(e)
       f32x16 sc[2];
       __builtin_amdgcn_s_setprio(1);
       if (e > 0) {
-        qk(st, sc);
-        pv(st_b);
+        qk(s_cur, sc);
+        pv(s_prv);
         m_order();
       } else {
-        qk(st, sc);
+        qk(s_cur, sc);
       }
       __builtin_amdgcn_s_setprio(0);
       if (grp == 1) wait_vmcnt<4>();  // V(e) must have landed; V(e+1) may still be in flight
@@ -380,7 +392,7 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       // a list refill (every 64 entries) is waited for here, which also waits for
       // this wave's tile loads in flight: group 0 needs K(e+1) now anyway
       wl.advance(e, lane);
-      issue(st_b, x2);
+      issue(s_prv, x2);
       if (grp == 0) wait_vmcnt<4>();  // K(e+1) must have landed; K(e+2) may still be in flight
       // pinned here, or the optimiser sinks the softmax below the barrier that ends
       // its phase, next to the products that consume P, and the two groups' vector
@@ -395,11 +407,14 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       lds_barrier();
       x0 = x1;
       x1 = x2;
-      st = st == 2 ? 0 : st + 1;
+      const uint32_t s_old = s_prv;
+      s_prv = s_cur;
+      s_cur = s_nxt;
+      s_nxt = s_old;
     }
     // M(n): the last product
     __builtin_amdgcn_s_setprio(1);
-    pv(st == 0 ? 2 : st - 1);
+    pv(s_prv);
     __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();  // the two loads past the end must land before the workgroup's LDS is released
     lds_barrier();
