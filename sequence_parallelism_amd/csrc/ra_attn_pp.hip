@@ -316,11 +316,13 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
         }
       }
       // online softmax in the log2 domain; the running max is exact
+      // IEEE maximum (v_maximum3_f32 on gfx950): unlike fmaxf it needs no
+      // canonicalising of the MFMA results; scores are finite or -inf here
       float mx = sc[0][0];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kt][i]);
+        for (int i = 0; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, sc[kt][i]);
       // a row that sees none of the tile: max -inf and P = exp2(-inf) = 0, through
       // an added -inf (arithmetic rather than a select, which the compiler turns
       // into a branch around the row maximum)
