@@ -377,7 +377,7 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
     for (int e = 0; e < n; ++e) {
       // M(e)
       f32x16 sc[2];
-      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(2);
       if (e > 0) {
         qk(s_cur, sc);
         pv(s_prv);
@@ -389,12 +389,13 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       if (grp == 1) wait_vmcnt<4>();  // V(e) must have landed; V(e+1) may still be in flight
       lds_barrier();
       // V(e)
+      // this group's tile of entry e + 2 is requested first, ahead of the softmax
       Ent x2 = fetch(e + 2);
+      issue(s_prv, x2);
       v_phase(sc, x0);
       // a list refill (every 64 entries) is waited for here, which also waits for
-      // this wave's tile loads in flight: group 0 needs K(e+1) now anyway
+      // this wave's tile loads in flight
       wl.advance(e, lane);
-      issue(s_prv, x2);
       if (grp == 0) wait_vmcnt<4>();  // K(e+1) must have landed; K(e+2) may still be in flight
       // pinned here, or the optimiser sinks the softmax below the barrier that ends
       // its phase, next to the products that consume P, and the two groups' vector
@@ -415,7 +416,7 @@ __global__ void __launch_bounds__(512, 1) ring_attn_pp_kernel(const AttnArgs a) 
       s_nxt = s_old;
     }
     // M(n): the last product
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(2);
     pv(s_prv);
     __builtin_amdgcn_s_setprio(0);
     wait_vmcnt<0>();  // the two loads past the end must land before the workgroup's LDS is released
