@@ -33,7 +33,7 @@ EXPORTS = ("ra_workspace_size", "ra_forward", "ra_plan", "ra_forward_planned", "
            "ra_backward_workspace_size", "ra_backward", "ra_lse_merge", "ra_classify",
            "ulysses_permute", "ulysses_permute_strided", "usp_workspace_size", "usp_forward",
            "cp_reorder", "cp_reorder_docs", "ra_local_length", "ra_doc_workspace_size",
-           "ra_status_string", "ra_abi_version")
+           "ra_status_string", "ra_abi_version", "ra_probe_mfma")
 
 
 class RAError(RuntimeError):
@@ -98,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.cp_reorder.restype = ctypes.c_int
     lib.ra_status_string.argtypes = [ctypes.c_int]
     lib.ra_status_string.restype = ctypes.c_char_p
+    lib.ra_probe_mfma.argtypes = [i32, i32, i32, vp, vp]
+    lib.ra_probe_mfma.restype = ctypes.c_int
     lib.ra_abi_version.argtypes = []
     lib.ra_abi_version.restype = i32
     _lib = lib
@@ -117,11 +119,71 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _torch_stream(stream):
+    """The torch stream object of `stream` (None: the current stream; a raw
+    hipStream_t handle is wrapped as an external stream)."""
     import torch
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    if int(stream) == 0:
+        return torch.cuda.default_stream()
+    return torch.cuda.ExternalStream(int(stream))
+
+
+class _On:
+    """Runs the body with `stream` as the current stream, so that the caching
+    allocator associates every temporary (workspace, default outputs) with the
+    stream the kernels run on: a temporary freed when the call returns is then
+    reused only by work ordered after those kernels."""
+
+    def __init__(self, stream):
+        import torch
+        self.s = _torch_stream(stream)
+        self.ctx = torch.cuda.stream(self.s)
+
+    def __enter__(self):
+        self.ctx.__enter__()
+        return self.s.cuda_stream
+
+    def __exit__(self, *exc):
+        return self.ctx.__exit__(*exc)
+
+
+def _need(t, name: str, shape, dtype=None, contiguous: bool = True):
+    """Raises ValueError unless tensor t has exactly `shape` (and `dtype`) and is contiguous."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(s) for s in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(s) for s in shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_bytes(t, name: str, nbytes: int):
+    """Raises ValueError unless t is a contiguous tensor of at least nbytes bytes."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, {nbytes} needed")
+
+
+def _same_gpu(*named):
+    """Raises ValueError unless every given tensor sits on one GPU device."""
+    ts = [(n, t) for n, t in named if t is not None]
+    dev = ts[0][1].device
+    if dev.type != "cuda":
+        raise ValueError(f"{ts[0][0]} is on {dev}: every tensor must be on a GPU")
+    for n, t in ts[1:]:
+        if t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, {ts[0][0]} on {dev}: tensors must share one GPU")
+    return dev
 
 
 def _dtype_code(dt) -> int:
@@ -131,6 +193,11 @@ def _dtype_code(dt) -> int:
     if dt == torch.float32:
         return RA_F32
     raise ValueError(f"unsupported dtype {dt}")
+
+
+def _torch_dtype(code: int):
+    import torch
+    return torch.bfloat16 if code == RA_BF16 else torch.float32
 
 
 def _part(partition) -> int:
@@ -169,26 +236,42 @@ def _global_len(partition, cp, s_l, cu_seqlens, s_total):
 
 def _attn_common(q, k, v, cp_size, causal, softmax_scale, out_dtype, partition="contiguous", cu_seqlens=None,
                  s_total=None):
-    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+    """Checks q [S_l,hq,d] and k, v [cp,S_l,hkv,d] against each other; returns the shape."""
+    if q is None or k is None or v is None:
+        raise ValueError("q, k and v are required")
+    if q.dim() != 3 or k.dim() != 4:
         raise ValueError("q must be [S_l, hq, d]; k, v must be [cp, S_l, hkv, d]")
     s_l, hq, d = q.shape
     cp, s_l2, hkv, d2 = k.shape
     if cp != cp_size or s_l2 != s_l or d2 != d:
-        raise ValueError("q / k / v shapes disagree")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous")
-    in_code = _dtype_code(q.dtype)
+        raise ValueError(f"k has shape {tuple(k.shape)}; expected [{cp_size}, {s_l}, hkv, {d}]")
+    _need(q, "q", q.shape)
+    in_dtype = q.dtype
+    _dtype_code(in_dtype)
+    _need(k, "k", k.shape, in_dtype)
+    _need(v, "v", k.shape, in_dtype)
     if out_dtype is None:
         out_dtype = q.dtype
     S = _global_len(partition, cp, s_l, cu_seqlens, s_total)
-    shape = make_shape(S, hq, hkv, d, causal, softmax_scale, in_code, _dtype_code(out_dtype))
+    if _part(partition) == PARTITIONS["doc_zigzag"]:
+        want = ra_local_length(S, cp_size, partition, cu_seqlens)
+        if want != s_l:
+            raise ValueError(f"doc_zigzag: this S and cu_seqlens give S_l = {want}, the tensors hold {s_l}")
+    elif S != cp * s_l:
+        raise ValueError(f"s_total {S} is not cp * S_l = {cp * s_l}")
+    shape = make_shape(S, hq, hkv, d, causal, softmax_scale, _dtype_code(in_dtype), _dtype_code(out_dtype))
     return shape, s_l, hq, d, out_dtype
 
 
-def _workspace(shape, cp_size, n_docs, device, workspace):
+def _check_ws(workspace, need: int):
+    """Checks a caller's workspace against `need` bytes (None: one is allocated later)."""
+    if workspace is not None:
+        _need_bytes(workspace, "workspace", need)
+
+
+def _workspace(need, device, workspace):
+    """The caller's (checked) workspace, or a new one on the current stream."""
     import torch
-    need = ra_workspace_size(shape, cp_size, n_docs)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
@@ -203,16 +286,37 @@ def ra_forward(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partit
     shape, s_l, hq, d, out_dtype = _attn_common(q, k, v, cp_size, causal, softmax_scale, out_dtype, partition,
                                                 cu_seqlens, s_total)
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
-    if out is None:
-        out = torch.empty((s_l, hq, d), dtype=out_dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((hq, s_l), dtype=torch.float32, device=q.device)
-    ws, ws_bytes = _workspace(shape, cp_size, n_docs, q.device, workspace)
-    st = load_library().ra_forward(_ptr(q), _ptr(k), _ptr(v), cu_ptr, n_docs, int(cp_size), int(rank),
-                                   _part(partition), ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(ws),
-                                   ws_bytes, _stream(stream))
-    _check(st, "ra_forward")
+    if out is not None:
+        _need(out, "out", (s_l, hq, d), out_dtype)
+    if lse is not None:
+        _need(lse, "lse", (hq, s_l), torch.float32)
+    need = ra_workspace_size(shape, cp_size, n_docs)
+    _check_ws(workspace, need)
+    dev = _same_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("workspace", workspace))
+    with _On(stream) as st:
+        if out is None:
+            out = torch.empty((s_l, hq, d), dtype=out_dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((hq, s_l), dtype=torch.float32, device=dev)
+        ws, ws_bytes = _workspace(need, dev, workspace)
+        status = load_library().ra_forward(_ptr(q), _ptr(k), _ptr(v), cu_ptr, n_docs, int(cp_size), int(rank),
+                                           _part(partition), ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(ws),
+                                           ws_bytes, st)
+    _check(status, "ra_forward")
     return out, lse
+
+
+def ra_probe_mfma(iters: int, workgroups: int, waves: int = 8, sink=None, stream=None):
+    """Calibration (include/ra_probe.h): `workgroups` x `waves` waves each run `iters`
+    x 4 independent bf16 MFMAs from registers. Returns the sink tensor; executed
+    FLOPs = workgroups * waves * iters * 4 * 32768."""
+    import torch
+    with _On(stream) as st:
+        if sink is None:
+            sink = torch.empty(int(workgroups) * int(waves) * 64, dtype=torch.float32, device="cuda")
+        status = load_library().ra_probe_mfma(int(iters), int(workgroups), int(waves), _ptr(sink), st)
+    _check(status, "ra_probe_mfma")
+    return sink
 
 
 class Plan:
@@ -226,32 +330,52 @@ class Plan:
 def ra_plan(s_total: int, hq: int, hkv: int, d: int, cu_seqlens=None, cp_size: int = 1, rank: int = 0,
             partition="contiguous", *, causal: bool = True, softmax_scale: float = 0.0, in_dtype=None,
             out_dtype=None, device="cuda", workspace=None, stream=None) -> Plan:
-    """Uploads cu_seqlens and builds the work list; returns a Plan for ra_forward_planned."""
+    """Uploads cu_seqlens and builds the work list; returns a Plan for ra_forward_planned.
+    The plan must be used on the stream it was built on (or after a synchronisation)."""
     import torch
     in_dtype = torch.bfloat16 if in_dtype is None else in_dtype
     out_dtype = in_dtype if out_dtype is None else out_dtype
     shape = make_shape(s_total, hq, hkv, d, causal, softmax_scale, _dtype_code(in_dtype), _dtype_code(out_dtype))
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
-    ws, ws_bytes = _workspace(shape, cp_size, n_docs, device, workspace)
-    st = load_library().ra_plan(ctypes.byref(shape), cu_ptr, n_docs, int(cp_size), int(rank), _part(partition),
-                                _ptr(ws), ws_bytes, _stream(stream))
-    _check(st, "ra_plan")
+    need = ra_workspace_size(shape, cp_size, n_docs)
+    _check_ws(workspace, need)
+    dev = torch.device(device) if workspace is None else _same_gpu(("workspace", workspace))
+    if dev.type != "cuda":
+        raise ValueError(f"device {dev}: the plan lives on a GPU")
+    with _On(stream) as st:
+        ws, ws_bytes = _workspace(need, dev, workspace)
+        status = load_library().ra_plan(ctypes.byref(shape), cu_ptr, n_docs, int(cp_size), int(rank),
+                                        _part(partition), _ptr(ws), ws_bytes, st)
+    _check(status, "ra_plan")
     return Plan(shape, n_docs, int(cp_size), int(rank), _part(partition), ws, ws_bytes)
 
 
 def ra_forward_planned(q, k, v, plan: Plan, *, out=None, lse=None, stream=None):
-    """The attention kernel alone, on a Plan from ra_plan with the same shape."""
+    """The attention kernel alone, on a Plan from ra_plan. q, k, v (and out, lse when
+    given) must match the plan's shape: q [S/cp, hq, d], k, v [cp, S/cp, hkv, d]."""
     import torch
-    s_l, hq, d = q.shape
-    out_dtype = torch.bfloat16 if plan.shape.out_dtype == RA_BF16 else torch.float32
-    if out is None:
-        out = torch.empty((s_l, hq, d), dtype=out_dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((hq, s_l), dtype=torch.float32, device=q.device)
-    st = load_library().ra_forward_planned(_ptr(q), _ptr(k), _ptr(v), plan.n_docs, plan.cp_size, plan.rank,
-                                           plan.partition, ctypes.byref(plan.shape), _ptr(out), _ptr(lse),
-                                           _ptr(plan.workspace), plan.ws_bytes, _stream(stream))
-    _check(st, "ra_forward_planned")
+    sh = plan.shape
+    if sh.s_total % plan.cp_size:
+        raise ValueError("plan: S not divisible by cp")
+    s_l = sh.s_total // plan.cp_size
+    in_dtype, out_dtype = _torch_dtype(sh.in_dtype), _torch_dtype(sh.out_dtype)
+    _need(q, "q", (s_l, sh.hq, sh.d), in_dtype)
+    _need(k, "k", (plan.cp_size, s_l, sh.hkv, sh.d), in_dtype)
+    _need(v, "v", (plan.cp_size, s_l, sh.hkv, sh.d), in_dtype)
+    if out is not None:
+        _need(out, "out", (s_l, sh.hq, sh.d), out_dtype)
+    if lse is not None:
+        _need(lse, "lse", (sh.hq, s_l), torch.float32)
+    dev = _same_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("plan workspace", plan.workspace))
+    with _On(stream) as st:
+        if out is None:
+            out = torch.empty((s_l, sh.hq, sh.d), dtype=out_dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((sh.hq, s_l), dtype=torch.float32, device=dev)
+        status = load_library().ra_forward_planned(_ptr(q), _ptr(k), _ptr(v), plan.n_docs, plan.cp_size, plan.rank,
+                                                   plan.partition, ctypes.byref(sh), _ptr(out), _ptr(lse),
+                                                   _ptr(plan.workspace), plan.ws_bytes, st)
+    _check(status, "ra_forward_planned")
     return out, lse
 
 
@@ -263,15 +387,24 @@ def ra_forward_steps(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, 
     shape, s_l, hq, d, _ = _attn_common(q, k, v, cp_size, causal, softmax_scale, torch.float32, partition,
                                         cu_seqlens, s_total)
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
-    if o_steps is None:
-        o_steps = torch.empty((cp_size, s_l, hq, d), dtype=torch.float32, device=q.device)
-    if lse_steps is None:
-        lse_steps = torch.empty((cp_size, hq, s_l), dtype=torch.float32, device=q.device)
-    ws, ws_bytes = _workspace(shape, cp_size, n_docs, q.device, workspace)
-    st = load_library().ra_forward_steps(_ptr(q), _ptr(k), _ptr(v), cu_ptr, n_docs, int(cp_size), int(rank),
-                                         _part(partition), ctypes.byref(shape), _ptr(o_steps), _ptr(lse_steps),
-                                         _ptr(ws), ws_bytes, _stream(stream))
-    _check(st, "ra_forward_steps")
+    if o_steps is not None:
+        _need(o_steps, "o_steps", (cp_size, s_l, hq, d), torch.float32)
+    if lse_steps is not None:
+        _need(lse_steps, "lse_steps", (cp_size, hq, s_l), torch.float32)
+    need = ra_workspace_size(shape, cp_size, n_docs)
+    _check_ws(workspace, need)
+    dev = _same_gpu(("q", q), ("k", k), ("v", v), ("o_steps", o_steps), ("lse_steps", lse_steps),
+                    ("workspace", workspace))
+    with _On(stream) as st:
+        if o_steps is None:
+            o_steps = torch.empty((cp_size, s_l, hq, d), dtype=torch.float32, device=dev)
+        if lse_steps is None:
+            lse_steps = torch.empty((cp_size, hq, s_l), dtype=torch.float32, device=dev)
+        ws, ws_bytes = _workspace(need, dev, workspace)
+        status = load_library().ra_forward_steps(_ptr(q), _ptr(k), _ptr(v), cu_ptr, n_docs, int(cp_size), int(rank),
+                                                 _part(partition), ctypes.byref(shape), _ptr(o_steps),
+                                                 _ptr(lse_steps), _ptr(ws), ws_bytes, st)
+    _check(status, "ra_forward_steps")
     return o_steps, lse_steps
 
 
@@ -287,43 +420,63 @@ def ra_backward(q, k, v, out, lse, dout, cu_seqlens=None, cp_size: int = 1, rank
     (dq fp32 [S_l,hq,d], dk fp32 [cp,S_l,hkv,d], dv fp32 [cp,S_l,hkv,d]): dk / dv hold
     this rank's contribution to every chunk's gradient."""
     import torch
+    if out is None:
+        raise ValueError("out is required")
     shape, s_l, hq, d, _ = _attn_common(q, k, v, cp_size, causal, softmax_scale, out.dtype, partition, cu_seqlens,
                                         s_total)
-    if dout.shape != q.shape or dout.dtype != q.dtype or out.shape != q.shape or lse.shape != (hq, s_l):
-        raise ValueError("out / dout must be [S_l,hq,d] (dout in q's dtype), lse [hq,S_l]")
-    for t in (out, lse, dout):
-        if not t.is_contiguous():
-            raise ValueError("out, lse, dout must be contiguous")
+    _need(out, "out", q.shape)
+    _need(lse, "lse", (hq, s_l), torch.float32)
+    _need(dout, "dout", q.shape, q.dtype)
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
     hkv = k.shape[2]
-    if dq is None:
-        dq = torch.empty((s_l, hq, d), dtype=torch.float32, device=q.device)
-    if dk is None:
-        dk = torch.empty((cp_size, s_l, hkv, d), dtype=torch.float32, device=q.device)
-    if dv is None:
-        dv = torch.empty((cp_size, s_l, hkv, d), dtype=torch.float32, device=q.device)
+    for name, t, shp in (("dq", dq, (s_l, hq, d)), ("dk", dk, (cp_size, s_l, hkv, d)),
+                         ("dv", dv, (cp_size, s_l, hkv, d))):
+        if t is not None:
+            _need(t, name, shp, torch.float32)
     need = ra_backward_workspace_size(shape, cp_size, n_docs)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    st = load_library().ra_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), cu_ptr, n_docs,
-                                    int(cp_size), int(rank), _part(partition), ctypes.byref(shape), _ptr(dq),
-                                    _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "ra_backward")
+    _check_ws(workspace, need)
+    dev = _same_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("dout", dout), ("dq", dq),
+                    ("dk", dk), ("dv", dv), ("workspace", workspace))
+    with _On(stream) as st:
+        if dq is None:
+            dq = torch.empty((s_l, hq, d), dtype=torch.float32, device=dev)
+        if dk is None:
+            dk = torch.empty((cp_size, s_l, hkv, d), dtype=torch.float32, device=dev)
+        if dv is None:
+            dv = torch.empty((cp_size, s_l, hkv, d), dtype=torch.float32, device=dev)
+        ws, ws_bytes = _workspace(need, dev, workspace)
+        status = load_library().ra_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), cu_ptr,
+                                            n_docs, int(cp_size), int(rank), _part(partition), ctypes.byref(shape),
+                                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes, st)
+    _check(status, "ra_backward")
     return dq, dk, dv
 
 
 def ra_lse_merge(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
-    """fp32 merge of two partials; o [rows,h,d], lse [h,rows]."""
+    """fp32 merge of two partials; o [rows,h,d], lse [h,rows]. o_out / lse_out may be
+    o_a or o_b / lse_a or lse_b (in place)."""
     import torch
+    if o_a is None or o_a.dim() != 3:
+        raise ValueError("o_a must be [rows, h, d]")
     rows, h, d = o_a.shape
-    if o_out is None:
-        o_out = torch.empty_like(o_a)
-    if lse_out is None:
-        lse_out = torch.empty_like(lse_a)
-    st = load_library().ra_lse_merge(rows, h, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out),
-                                     _ptr(lse_out), _stream(stream))
-    _check(st, "ra_lse_merge")
+    _need(o_a, "o_a", (rows, h, d), torch.float32)
+    _need(o_b, "o_b", (rows, h, d), torch.float32)
+    _need(lse_a, "lse_a", (h, rows), torch.float32)
+    _need(lse_b, "lse_b", (h, rows), torch.float32)
+    if o_out is not None:
+        _need(o_out, "o_out", (rows, h, d), torch.float32)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", (h, rows), torch.float32)
+    dev = _same_gpu(("o_a", o_a), ("lse_a", lse_a), ("o_b", o_b), ("lse_b", lse_b), ("o_out", o_out),
+                    ("lse_out", lse_out))
+    with _On(stream) as st:
+        if o_out is None:
+            o_out = torch.empty_like(o_a)
+        if lse_out is None:
+            lse_out = torch.empty_like(lse_a)
+        status = load_library().ra_lse_merge(rows, h, d, _ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b),
+                                             _ptr(o_out), _ptr(lse_out), st)
+    _check(status, "ra_lse_merge")
     return o_out, lse_out
 
 
@@ -343,25 +496,35 @@ def cp_reorder_docs(x, cp_size: int, cu_seqlens=None, inverse: bool = False, out
     """Per-document zigzag reorder. Forward: [S, h, d] -> [cp, S_l, h, d] (padding zero);
     inverse: [cp, S_l, h, d] -> [S, h, d] (pass s_total when cu_seqlens is None)."""
     import torch
-    if not x.is_contiguous():
-        raise ValueError("input must be contiguous")
+    if x is None or x.dim() != (4 if inverse else 3):
+        raise ValueError("input must be [S, h, d] (forward) or [cp, S_l, h, d] (inverse)")
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
     if not inverse:
         s, h, d = x.shape
     else:
         _, _, h, d = x.shape
+        if cu_arr is None and s_total is None:
+            raise ValueError("the inverse needs cu_seqlens or s_total")
         s = int(cu_arr[-1]) if cu_arr is not None else int(s_total)
     sl = ra_local_length(s, cp_size, "doc_zigzag", cu_seqlens)
-    if out is None:
-        shape_out = (s, h, d) if inverse else (cp_size, sl, h, d)
-        out = torch.empty(shape_out, dtype=x.dtype, device=x.device)
-    if workspace is None:
-        workspace = torch.empty(max(256, ra_doc_workspace_size(s, cp_size, cu_seqlens)), dtype=torch.uint8,
-                                device=x.device)
-    st = load_library().cp_reorder_docs(_ptr(x), _ptr(out), int(s), int(h), int(d), x.element_size(), int(cp_size),
-                                        cu_ptr, n_docs, int(bool(inverse)), _ptr(workspace),
-                                        workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(st, "cp_reorder_docs")
+    if sl < 0:
+        raise ValueError(f"doc_zigzag: S={s}, cp={cp_size} and cu_seqlens give no valid layout")
+    shape_in = (cp_size, sl, h, d) if inverse else (s, h, d)
+    shape_out = (s, h, d) if inverse else (cp_size, sl, h, d)
+    _need(x, "input", shape_in)
+    if out is not None:
+        _need(out, "out", shape_out, x.dtype)
+    need = ra_doc_workspace_size(s, cp_size, cu_seqlens)
+    _check_ws(workspace, need)
+    dev = _same_gpu(("input", x), ("out", out), ("workspace", workspace))
+    with _On(stream) as st:
+        if out is None:
+            out = torch.empty(shape_out, dtype=x.dtype, device=dev)
+        ws, ws_bytes = _workspace(need, dev, workspace)
+        status = load_library().cp_reorder_docs(_ptr(x), _ptr(out), int(s), int(h), int(d), x.element_size(),
+                                                int(cp_size), cu_ptr, n_docs, int(bool(inverse)), _ptr(ws), ws_bytes,
+                                                st)
+    _check(status, "cp_reorder_docs")
     return out
 
 
@@ -373,35 +536,50 @@ def ra_classify(s_total: int, cp_size: int, rank: int, partition, bm: int, bn: i
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
     s_l = ra_local_length(s_total, cp_size, partition, cu_seqlens)
     if s_l < 0:
-        s_l = s_total // cp_size  # invalid arguments: the call below reports the status
-    cls = torch.empty((cp_size, -(-s_l // bm), -(-s_l // bn)), dtype=torch.int8, device=device)
+        s_l = s_total // max(1, cp_size)  # invalid arguments: the call below reports the status
+    if bm < 1 or bn < 1:
+        raise ValueError("bm and bn must be positive")
+    dev = torch.device(device)
+    if dev.type != "cuda":
+        raise ValueError(f"device {dev}: classification runs on a GPU")
     need = ra_doc_workspace_size(s_total, cp_size, cu_seqlens) if _part(partition) == PARTITIONS["doc_zigzag"] else 0
-    ws = torch.empty(max(256, 4 * (n_docs + 1), need), dtype=torch.uint8, device=device)
-    st = load_library().ra_classify(ctypes.byref(shape), cu_ptr, n_docs, int(cp_size), int(rank), _part(partition),
-                                    int(bm), int(bn), _ptr(cls), _ptr(ws), ws.numel(), _stream(stream))
-    _check(st, "ra_classify")
+    with _On(stream) as st:
+        cls = torch.empty((cp_size, -(-s_l // bm), -(-s_l // bn)), dtype=torch.int8, device=dev)
+        ws = torch.empty(max(256, 4 * (n_docs + 1), need), dtype=torch.uint8, device=dev)
+        status = load_library().ra_classify(ctypes.byref(shape), cu_ptr, n_docs, int(cp_size), int(rank),
+                                            _part(partition), int(bm), int(bn), _ptr(cls), _ptr(ws), ws.numel(), st)
+    _check(status, "ra_classify")
     return cls
 
 
 def ulysses_permute(x, n: int, inverse: bool = False, out=None, stream=None):
     """Forward: [n, s_l, h, d] -> [n, n*s_l, h/n, d]; inverse: the reverse."""
     import torch
-    if not x.is_contiguous():
-        raise ValueError("input must be contiguous")
+    if x is None or x.dim() != 4:
+        raise ValueError("input must be 4-d: [n, s_l, h, d] (forward) or [n, n*s_l, h/n, d] (inverse)")
     if not inverse:
         nn, s_l, h, d = x.shape
-        shape_out = (nn, nn * s_l, h // max(1, n), d)
+        if n < 1 or h % n:
+            raise ValueError(f"the head count {h} must divide by n = {n}")
+        shape_out = (nn, nn * s_l, h // n, d)
     else:
         nn, s, hn, d = x.shape
-        s_l, h = s // max(1, n), hn * n
+        if n < 1 or s % n:
+            raise ValueError(f"the token count {s} must divide by n = {n}")
+        s_l, h = s // n, hn * n
         shape_out = (nn, s_l, h, d)
     if nn != n:
         raise ValueError("leading dimension must equal n")
-    if out is None:
-        out = torch.empty(shape_out, dtype=x.dtype, device=x.device)
-    st = load_library().ulysses_permute(_ptr(x), _ptr(out), int(n), int(s_l), int(h), int(d), x.element_size(),
-                                        int(bool(inverse)), _stream(stream))
-    _check(st, "ulysses_permute")
+    _need(x, "input", x.shape)
+    if out is not None:
+        _need(out, "out", shape_out, x.dtype)
+    dev = _same_gpu(("input", x), ("out", out))
+    with _On(stream) as st:
+        if out is None:
+            out = torch.empty(shape_out, dtype=x.dtype, device=dev)
+        status = load_library().ulysses_permute(_ptr(x), _ptr(out), int(n), int(s_l), int(h), int(d),
+                                                x.element_size(), int(bool(inverse)), st)
+    _check(status, "ulysses_permute")
     return out
 
 
@@ -409,18 +587,32 @@ def ulysses_permute_strided(x, n: int, out, block_stride: int, inverse: bool = F
                             stream=None):
     """ulysses_permute with the head-split side's n blocks block_stride bytes apart.
     Forward: x [n, s_l, h, d] -> blocks of out; inverse: blocks of x -> out [n, s_l, h, d].
-    `out` (forward) or `x` (inverse) is the base tensor of the strided side; for the
-    inverse pass the full head count h."""
-    if not inverse:
-        nn, s_l, hh, d = x.shape
-    else:
-        nn, s_l, hh, d = out.shape
+    `out` (forward) or `x` (inverse) is the base tensor of the strided side, and must
+    hold the n blocks: (n - 1) block_stride bytes plus one block."""
+    if x is None or out is None:
+        raise ValueError("x and out are required")
+    packed = out if inverse else x
+    if packed.dim() != 4:
+        raise ValueError("the packed side must be [n, s_l, h, d]")
+    nn, s_l, hh, d = packed.shape
     if nn != n:
         raise ValueError("leading dimension must equal n")
-    st = load_library().ulysses_permute_strided(_ptr(x), _ptr(out), int(n), int(s_l), int(hh), int(d),
-                                                x.element_size(), int(bool(inverse)), int(block_stride),
-                                                _stream(stream))
-    _check(st, "ulysses_permute_strided")
+    if n < 1 or hh % n:
+        raise ValueError(f"the head count {hh} must divide by n = {n}")
+    strided = x if inverse else out
+    if strided.dtype != packed.dtype:
+        raise ValueError("x and out must share a dtype")
+    _need(packed, "out" if inverse else "x", packed.shape)
+    block = n * s_l * (hh // n) * d * packed.element_size()
+    if block_stride < block:
+        raise ValueError(f"block_stride {block_stride} is smaller than one block ({block} bytes)")
+    _need_bytes(strided, "x" if inverse else "out", (n - 1) * int(block_stride) + block)
+    _same_gpu(("x", x), ("out", out))
+    with _On(stream) as st:
+        status = load_library().ulysses_permute_strided(_ptr(x), _ptr(out), int(n), int(s_l), int(hh), int(d),
+                                                        packed.element_size(), int(bool(inverse)),
+                                                        int(block_stride), st)
+    _check(status, "ulysses_permute_strided")
     return out
 
 
@@ -434,48 +626,66 @@ def usp_forward(q, k, v, cu_seqlens=None, ulysses: int = 1, ring: int = 1, parti
     """Ulysses x Ring grid on one GPU. q [ring, ulysses, S/(ring ulysses), hq, d]; k, v the same with hkv.
     Returns (out [ring, ulysses, S/(ring ulysses), hq, d], lse fp32 [ulysses, ring, hq/ulysses, S/ring])."""
     import torch
-    if q.dim() != 5 or k.dim() != 5 or v.shape != k.shape:
+    if q is None or k is None or v is None or q.dim() != 5 or k.dim() != 5:
         raise ValueError("q, k, v must be [ring, ulysses, S/(ring ulysses), heads, d]")
     R, U, sh, hq, d = q.shape
     hkv = k.shape[3]
     if (R, U, sh) != tuple(k.shape[:3]) or R != ring or U != ulysses or k.shape[4] != d:
         raise ValueError("q / k / v shapes disagree with the grid")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous")
+    if hq % U or hkv % U:
+        raise ValueError(f"the head counts {hq}, {hkv} must divide by ulysses = {U}")
+    _dtype_code(q.dtype)
+    _need(q, "q", q.shape)
+    _need(k, "k", k.shape, q.dtype)
+    _need(v, "v", k.shape, q.dtype)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     S = R * U * sh
     shape = make_shape(S, hq, hkv, d, causal, softmax_scale, _dtype_code(q.dtype), _dtype_code(out_dtype))
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
-    if out is None:
-        out = torch.empty((R, U, sh, hq, d), dtype=out_dtype, device=q.device)
-    if lse is None:
-        lse = torch.empty((U, R, hq // max(1, U), S // R), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = torch.empty(max(256, usp_workspace_size(shape, U, R, n_docs)), dtype=torch.uint8,
-                                device=q.device)
-    st = load_library().usp_forward(_ptr(q), _ptr(k), _ptr(v), cu_ptr, n_docs, int(U), int(R), _part(partition),
-                                    ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(st, "usp_forward")
+    if out is not None:
+        _need(out, "out", (R, U, sh, hq, d), out_dtype)
+    if lse is not None:
+        _need(lse, "lse", (U, R, hq // U, S // R), torch.float32)
+    need = usp_workspace_size(shape, U, R, n_docs)
+    _check_ws(workspace, need)
+    dev = _same_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("workspace", workspace))
+    with _On(stream) as st:
+        if out is None:
+            out = torch.empty((R, U, sh, hq, d), dtype=out_dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((U, R, hq // U, S // R), dtype=torch.float32, device=dev)
+        ws, ws_bytes = _workspace(need, dev, workspace)
+        status = load_library().usp_forward(_ptr(q), _ptr(k), _ptr(v), cu_ptr, n_docs, int(U), int(R),
+                                            _part(partition), ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(ws),
+                                            ws_bytes, st)
+    _check(status, "usp_forward")
     return out, lse
 
 
 def cp_reorder(x, cp_size: int, partition, inverse: bool = False, out=None, stream=None):
     """Forward: [S, h, d] -> [cp, S/cp, h, d]; inverse: the reverse."""
     import torch
-    if not x.is_contiguous():
-        raise ValueError("input must be contiguous")
+    if x is None or x.dim() != (4 if inverse else 3):
+        raise ValueError("input must be [S, h, d] (forward) or [cp, S/cp, h, d] (inverse)")
     if not inverse:
         s, h, d = x.shape
+        if cp_size < 1 or s % cp_size:
+            raise ValueError(f"S = {s} must divide by cp = {cp_size}")
         shape_out = (cp_size, s // cp_size, h, d)
     else:
         cp, s_l, h, d = x.shape
+        if cp != cp_size:
+            raise ValueError(f"leading dimension {cp} must equal cp = {cp_size}")
         s = cp * s_l
         shape_out = (s, h, d)
-    if out is None:
-        out = torch.empty(shape_out, dtype=x.dtype, device=x.device)
-    st = load_library().cp_reorder(_ptr(x), _ptr(out), int(s), int(h), int(d), x.element_size(), int(cp_size),
-                                   _part(partition), int(bool(inverse)), _stream(stream))
-    _check(st, "cp_reorder")
+    _need(x, "input", x.shape)
+    if out is not None:
+        _need(out, "out", shape_out, x.dtype)
+    dev = _same_gpu(("input", x), ("out", out))
+    with _On(stream) as st:
+        if out is None:
+            out = torch.empty(shape_out, dtype=x.dtype, device=dev)
+        status = load_library().cp_reorder(_ptr(x), _ptr(out), int(s), int(h), int(d), x.element_size(),
+                                           int(cp_size), _part(partition), int(bool(inverse)), st)
+    _check(status, "cp_reorder")
     return out

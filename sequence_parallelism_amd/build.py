@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libra.so")
-SOURCES = ["ra_api.hip", "ra_attn.hip", "ra_attn_pp.hip", "ra_aux.hip", "ra_bwd.hip", "ra_host.cpp"]
+SOURCES = ["ra_api.hip", "ra_attn.hip", "ra_attn_pp.hip", "ra_aux.hip", "ra_bwd.hip", "ra_probe.hip", "ra_host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -194,7 +194,7 @@ ra_status run_backward(const void* q, const void* k, const void* v, const void* 
 
 extern "C" {
 
-int32_t ra_abi_version(void) { return 1; }
+int32_t ra_abi_version(void) { return 2; }
 
 const char* ra_status_string(ra_status s) {
   switch (s) {

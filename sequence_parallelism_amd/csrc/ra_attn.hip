@@ -387,8 +387,11 @@ __global__ void __launch_bounds__(64) ring_attn_f32_kernel(const AttnArgs a) {
     float mx = -INFINITY;
     for (int j = 0; j < BN; ++j) {
       float dot = 0.f;
+      // the query row is read from LDS for every key: kept in registers beside the
+      // D accumulators it makes the per-step variant spill at head_dim 128
+      const int ql = opaque(lane);
 #pragma unroll
-      for (int c = 0; c < D; ++c) dot = __builtin_fmaf(qs[lane][c], ks[j][c], dot);
+      for (int c = 0; c < D; ++c) dot = __builtin_fmaf(qs[ql][c], ks[j][c], dot);
       const bool vis = ((unsigned)(j - tm.i0a) < (unsigned)tm.la) | ((unsigned)(j - tm.i0b) < (unsigned)tm.lb);
       s[j] = vis ? dot : -INFINITY;
       mx = fmaxf(mx, s[j]);

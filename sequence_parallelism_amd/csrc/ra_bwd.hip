@@ -630,11 +630,17 @@ __global__ void __launch_bounds__(256, 1) ring_bwd_dkv_bf16_kernel(const BwdArgs
 
 // ---------------------------------------------------------------------------
 // fp32 inputs, VALU path. dQ: one wave, one query row per lane, the forward's
-// fp32 work list (key tiles of 32 staged in LDS).
+// fp32 work list (key tiles of 32 staged in LDS). A workgroup accumulates
+// kBwdF32Cols of the D output columns (blockIdx.x % (D / kBwdF32Cols) picks
+// which), so that the per-lane accumulator stays in registers at head_dim 128;
+// the scores and dP still take the full dot products over D.
 // ---------------------------------------------------------------------------
+constexpr int kBwdF32Cols = 64;
+
 template <int D>
 __global__ void __launch_bounds__(64) ring_bwd_dq_f32_kernel(const BwdArgs a) {
   constexpr int BM = kAttnF32BM, BN = kAttnF32BN;
+  constexpr int DC = D < kBwdF32Cols ? D : kBwdF32Cols, NH = D / DC;
   static_assert(BM == 64, "one query row per lane");
   __shared__ float qs[BM][D + 1];
   __shared__ float gs[BM][D + 1];
@@ -642,9 +648,10 @@ __global__ void __launch_bounds__(64) ring_bwd_dq_f32_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float vs[BN][D];
 
   const int lane = threadIdx.x;
-  const int qt = a.order[blockIdx.x / a.hq];
+  const int c0 = (int)(blockIdx.x % NH) * DC, bid = (int)(blockIdx.x / NH);
+  const int qt = a.order[bid / a.hq];
   if (qt < 0 || qt >= a.nqt) return;
-  const int h = blockIdx.x % a.hq;
+  const int h = bid % a.hq;
   const int g = h / (a.hq / a.hkv);
   const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
   const int row = qt * BM + lane;
@@ -666,9 +673,9 @@ __global__ void __launch_bounds__(64) ring_bwd_dq_f32_kernel(const BwdArgs a) {
     dsum = a.dsum[(size_t)h * a.s_local + row];
     row_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, a.rank, row), lo, hi);
   }
-  float acc[D];
+  float acc[DC];
 #pragma unroll
-  for (int c = 0; c < D; ++c) acc[c] = 0.f;
+  for (int c = 0; c < DC; ++c) acc[c] = 0.f;
   const size_t kv_row = (size_t)a.hkv * D;
   const size_t kv_chunk = (size_t)a.s_local * kv_row;
   const int n_ent = clamp_count(a.wl_count[qt], a.wl_stride);
@@ -709,21 +716,24 @@ __global__ void __launch_bounds__(64) ring_bwd_dq_f32_kernel(const BwdArgs a) {
       const bool vis = ((unsigned)(j - tm.i0a) < (unsigned)tm.la) | ((unsigned)(j - tm.i0b) < (unsigned)tm.lb);
       const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s, C, -lse2)) : 0.f;
       const float ds = p * (dp - dsum);
+      const int jj = opaque(j);  // read again: see the dK/dV kernel
 #pragma unroll
-      for (int c = 0; c < D; ++c) acc[c] = __builtin_fmaf(ds, ks[j][c], acc[c]);
+      for (int c = 0; c < DC; ++c) acc[c] = __builtin_fmaf(ds, ks[jj][c0 + c], acc[c]);
     }
   }
   if (row_ok) {
-    float* dq = a.dq + ((size_t)row * a.hq + h) * D;
-    for (int c = 0; c < D; ++c) dq[c] = acc[c] * a.scale;
+    float* dq = a.dq + ((size_t)row * a.hq + h) * D + c0;
+    for (int c = 0; c < DC; ++c) dq[c] = acc[c] * a.scale;
   }
 }
 
 // dK and dV, fp32 VALU path: one wave, one key per lane (64 keys of one chunk
-// and one KV head), query tiles of 32 rows staged in LDS.
+// and one KV head), query tiles of 32 rows staged in LDS; kBwdF32Cols of the D
+// output columns per workgroup, as in the dQ kernel.
 template <int D>
 __global__ void __launch_bounds__(64) ring_bwd_dkv_f32_kernel(const BwdArgs a) {
   constexpr int BK = kBwdF32BK, BQ = kBwdF32BQ;
+  constexpr int DC = D < kBwdF32Cols ? D : kBwdF32Cols, NH = D / DC;
   static_assert(BK == 64, "one key per lane");
   __shared__ float ks[BK][D + 1];
   __shared__ float vs[BK][D + 1];
@@ -733,9 +743,10 @@ __global__ void __launch_bounds__(64) ring_bwd_dkv_f32_kernel(const BwdArgs a) {
 
   const int lane = threadIdx.x;
   const int n_kt = a.cp * a.nkt_kv;
-  const int kt = a.korder[blockIdx.x / a.hkv];
+  const int c0 = (int)(blockIdx.x % NH) * DC, bid = (int)(blockIdx.x / NH);
+  const int kt = a.korder[bid / a.hkv];
   if (kt < 0 || kt >= n_kt) return;
-  const int g = blockIdx.x % a.hkv;
+  const int g = bid % a.hkv;
   const int G = a.hq / a.hkv;
   const int owner = kt / a.nkt_kv, J = kt - owner * a.nkt_kv;
   const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
@@ -753,9 +764,9 @@ __global__ void __launch_bounds__(64) ring_bwd_dkv_f32_kernel(const BwdArgs a) {
   }
   int plo = 1, phi = 0;
   if (key_ok) key_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, owner, key), plo, phi);
-  float dk[D], dv[D];
+  float dk[DC], dv[DC];
 #pragma unroll
-  for (int c = 0; c < D; ++c) dk[c] = dv[c] = 0.f;
+  for (int c = 0; c < DC; ++c) dk[c] = dv[c] = 0.f;
   const int n_ent = clamp_count(a.kwl_count[kt], a.kwl_stride);
   const int* list = a.kwl + (size_t)kt * a.kwl_stride;
   const size_t q_row = (size_t)a.hq * D;
@@ -795,24 +806,30 @@ __global__ void __launch_bounds__(64) ring_bwd_dkv_f32_kernel(const BwdArgs a) {
     const TileMask tm = tile_mask(pinfo, a.rank, qa, qb, cls, key_ok, plo, phi);
     for (int r = 0; r < BQ; ++r) {
       float s = 0.f, dp = 0.f;
-#pragma unroll
+      // the lane's key row is read from LDS for every query row: kept opaque, the
+      // optimiser would hold all 2 D values in registers beside dK and dV and spill
+      const int kl = opaque(lane);
+#pragma unroll 16
       for (int c = 0; c < D; ++c) {
-        s = __builtin_fmaf(qs[r][c], ks[lane][c], s);
-        dp = __builtin_fmaf(gs[r][c], vs[lane][c], dp);
+        s = __builtin_fmaf(qs[r][c], ks[kl][c], s);
+        dp = __builtin_fmaf(gs[r][c], vs[kl][c], dp);
       }
       const bool vis = ((unsigned)(r - tm.i0a) < (unsigned)tm.la) | ((unsigned)(r - tm.i0b) < (unsigned)tm.lb);
       const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s, C, -l2s[r])) : 0.f;
       const float ds = p * (dp - dss[r]);
+      // the row is read again rather than kept from the dot products above (up to
+      // 2 D more live registers)
+      const int rr = opaque(r);
 #pragma unroll
-      for (int c = 0; c < D; ++c) {
-        dk[c] = __builtin_fmaf(ds, qs[r][c], dk[c]);
-        dv[c] = __builtin_fmaf(p, gs[r][c], dv[c]);
+      for (int c = 0; c < DC; ++c) {
+        dk[c] = __builtin_fmaf(ds, qs[rr][c0 + c], dk[c]);
+        dv[c] = __builtin_fmaf(p, gs[rr][c0 + c], dv[c]);
       }
     }
   }
   if (key_ok) {
-    const size_t base = ((size_t)owner * a.s_local + key) * kv_row + (size_t)g * D;
-    for (int c = 0; c < D; ++c) {
+    const size_t base = ((size_t)owner * a.s_local + key) * kv_row + (size_t)g * D + c0;
+    for (int c = 0; c < DC; ++c) {
       a.dk[base + c] = dk[c] * a.scale;
       a.dv[base + c] = dv[c];
     }
@@ -910,11 +927,12 @@ static hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
 
 template <int D>
 static hipError_t launch_bwd_f32(const BwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((ring_bwd_dq_f32_kernel<D>), dim3((unsigned)a.nqt * (unsigned)a.hq), dim3(64), 0, st, a);
+  constexpr unsigned NH = D < kBwdF32Cols ? 1 : D / kBwdF32Cols;  // column groups per row or key
+  hipLaunchKernelGGL((ring_bwd_dq_f32_kernel<D>), dim3((unsigned)a.nqt * (unsigned)a.hq * NH), dim3(64), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ring_bwd_dkv_f32_kernel<D>), dim3((unsigned)(a.cp * a.nkt_kv) * (unsigned)a.hkv), dim3(64), 0,
-                     st, a);
+  hipLaunchKernelGGL((ring_bwd_dkv_f32_kernel<D>), dim3((unsigned)(a.cp * a.nkt_kv) * (unsigned)a.hkv * NH), dim3(64),
+                     0, st, a);
   return hipGetLastError();
 }
 

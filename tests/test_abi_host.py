@@ -19,9 +19,14 @@ def _lib():
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "ra.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(\w+)\s*\(", src, flags=re.M))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(\w+)\s*\(", src, flags=re.M))
+    return names
 
 
 def test_library_exports_every_declared_symbol():
@@ -30,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     assert names == set(ra.EXPORTS), names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.ra_abi_version() == 1
+    assert lib.ra_abi_version() == 2
 
 
 def test_status_strings():
@@ -242,3 +247,11 @@ def test_doc_zigzag_validation_and_lengths():
     assert lib.cp_reorder_docs(P, P2, 512, 2, 128, 2, 4, arr, 4, 0, P, 64, None) == ra.RA_ERR_WORKSPACE
     # the forward's workspace size covers the doc-zigzag layout
     assert fwd(sh, cu=cu, n_docs=4, part=3, ws_bytes=ra.ra_workspace_size(sh, 4, 4) - 1, q=None) == ra.RA_ERR_NULL
+
+
+def test_probe_validation_codes():
+    lib = _lib()
+    assert lib.ra_probe_mfma(10, 4, 8, None, None) == ra.RA_ERR_NULL
+    assert lib.ra_probe_mfma(0, 4, 8, P, None) == ra.RA_ERR_SHAPE
+    assert lib.ra_probe_mfma(10, 0, 8, P, None) == ra.RA_ERR_SHAPE
+    assert lib.ra_probe_mfma(10, 4, 6, P, None) == ra.RA_ERR_SHAPE

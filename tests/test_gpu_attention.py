@@ -193,3 +193,32 @@ def test_prescaled_input_reading():
     """The alternative reading of 'N(0,1)/sqrt(128) scale': inputs pre-scaled by 1/sqrt(128)."""
     g = _case_inputs(2048, 4, 4, 128, "bf16", seed=21, prescale=1 / np.sqrt(128))
     _check_rank(g, 4, 0, "zigzag")
+
+
+def test_side_stream_launch_matches_the_current_stream():
+    """A call on a non-current stream allocates its workspace and default outputs on
+    that stream: the caching allocator may hand the freed workspace only to work
+    ordered after the kernels. Right after the call, the current stream allocates and
+    overwrites memory while the side stream may still read its plan; the side-stream
+    result must equal a current-stream run bit for bit."""
+    g = _case_inputs(8192, 8, 2, 128, "bf16", seed=23, docs="loguniform")
+    cp, rank, part = 4, 2, "zigzag"
+    qr, kr, vr = rank_inputs(g, cp, rank, part)
+    ref_o, ref_l = ra.ra_forward(qr, kr, vr, g.cu_seqlens, cp, rank, part, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        o, l = ra.ra_forward(qr, kr, vr, g.cu_seqlens, cp, rank, part, out_dtype=torch.float32, stream=side)
+        outs.append((o, l))
+        junk = [torch.full((1 << 20,), -1, dtype=torch.int32, device="cuda") for _ in range(8)]
+        del junk
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+    # a raw hipStream_t handle is accepted as well
+    o, l = ra.ra_forward(qr, kr, vr, g.cu_seqlens, cp, rank, part, out_dtype=torch.float32,
+                         stream=side.cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(l, ref_l)

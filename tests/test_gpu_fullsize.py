@@ -18,86 +18,125 @@ from tests.gpu_common import (TOL_LSE_BF16, TOL_O_BF16, device_bits, max_abs, or
 pytestmark = pytest.mark.gpu
 
 
+def _nan_outputs(s_l, hq, d, out_dtype):
+    """Outputs filled with NaN before the call, so that a row the kernel leaves
+    unwritten fails the all-rows finiteness check."""
+    out = torch.full((s_l, hq, d), float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full((hq, s_l), float("nan"), dtype=torch.float32, device="cuda")
+    return out, lse
+
+
 def _check_sampled(g, w, rank, rows, gq, gk, gv, out_dtype=torch.float32):
     qr, kr, vr = rank_inputs(g, w.cp, rank, w.partition)
-    out, lse = ra.ra_forward(qr, kr, vr, g.cu_seqlens, w.cp, rank, w.partition, out_dtype=out_dtype)
+    out, lse = _nan_outputs(qr.shape[0], w.hq, w.d, out_dtype)
+    print(f"{w.name} rank {rank} out {out_dtype} rows {len(rows)}", flush=True)
+    ra.ra_forward(qr, kr, vr, g.cu_seqlens, w.cp, rank, w.partition, out=out, lse=lse)
     torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()), "non-finite (unwritten) output"
+    assert bool(torch.isfinite(lse).all()), "non-finite (unwritten) LSE"
     O, L = oracle.attention_rank(gq, gk, gv, g.cu_seqlens, w.cp, rank, w.partition, rows=rows)
     o = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
     l = lse[:, torch.from_numpy(rows).cuda()].cpu().numpy()
     eo, el = max_abs(o, O), max_abs(l, L)
-    assert np.all(np.isfinite(out.float().cpu().numpy()))
     assert eo <= TOL_O_BF16 and el <= TOL_LSE_BF16, f"rank {rank}: max-abs O {eo:.3e} LSE {el:.3e}"
     return eo, el
 
 
-@pytest.fixture(scope="module")
-def llama7b():
-    g = synth.make_global_inputs(synth.LLAMA7B_ZIGZAG, 0)
-    return g, oracle_inputs(g)
+_CACHE = {}
 
 
+def _inputs(w, seed):
+    """Seeded global inputs of a workload and their fp64 view (one workload kept at a time)."""
+    key = (w.name, seed)
+    if key not in _CACHE:
+        _CACHE.clear()
+        g = synth.make_global_inputs(w, seed)
+        _CACHE[key] = (g, oracle_inputs(g))
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("rank", [0, 3])
-def test_llama7b_zigzag_sampled(llama7b, rank):
-    g, (gq, gk, gv) = llama7b
+def test_llama7b_zigzag_sampled(seed, rank):
     w = synth.LLAMA7B_ZIGZAG
-    rows = sample_rows(w.s_total // w.cp, extra=(4095, 4096, 127, 128, 8191), seed=rank)
-    _check_sampled(g, w, rank, rows, gq, gk, gv)
+    g, (gq, gk, gv) = _inputs(w, seed)
+    rows = sample_rows(w.s_total // w.cp, extra=(4095, 4096, 127, 128, 8191), n_random=32, seed=rank + 10 * seed)
+    _check_sampled(g, w, rank, rows, gq, gk, gv, out_dtype=torch.bfloat16 if seed == 1 else torch.float32)
 
 
-def test_llama7b_zigzag_bf16_output(llama7b):
-    g, (gq, gk, gv) = llama7b
-    w = synth.LLAMA7B_ZIGZAG
-    _check_sampled(g, w, 0, sample_rows(8192, seed=5), gq, gk, gv, out_dtype=torch.bfloat16)
-
-
-def test_gqa_striped_sampled():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gqa_striped_sampled(seed):
     w = synth.GQA_STRIPED
-    g = synth.make_global_inputs(w, 0)
-    gq, gk, gv = oracle_inputs(g)
+    g, (gq, gk, gv) = _inputs(w, seed)
     for rank in (0, 7):
-        _check_sampled(g, w, rank, sample_rows(w.s_total // w.cp, seed=rank), gq, gk, gv)
+        rows = sample_rows(w.s_total // w.cp, n_random=32, seed=rank + 10 * seed)
+        _check_sampled(g, w, rank, rows, gq, gk, gv, out_dtype=torch.bfloat16 if seed == 2 else torch.float32)
 
 
-def test_packed_documents_all_ranks_sampled():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_packed_documents_all_ranks_sampled(seed):
     w = synth.PACKED_ZIGZAG
-    g = synth.make_global_inputs(w, 0)
-    gq, gk, gv = oracle_inputs(g)
+    g, (gq, gk, gv) = _inputs(w, seed)
     cu = g.cu_seqlens
     for rank in range(w.cp):
         pos = oracle.positions(w.partition, w.s_total, w.cp, rank)
         # rows at document starts / ends that this rank holds
         idx = np.searchsorted(pos, np.concatenate([cu[1:-1] - 1, cu[1:-1]]))
-        rows = sample_rows(w.s_total // w.cp, extra=idx[:12], n_random=8, seed=rank)
-        _check_sampled(g, w, rank, rows, gq, gk, gv)
+        idx = idx[(idx < len(pos))]
+        rows = sample_rows(w.s_total // w.cp, extra=idx[:16], n_random=8, seed=rank + 10 * seed)
+        _check_sampled(g, w, rank, rows, gq, gk, gv,
+                       out_dtype=torch.bfloat16 if (seed == 1 and rank % 2) else torch.float32)
 
 
-def test_ulysses_path_sampled():
+def _ulysses_device_check(x3, n, H, d, dev, rows, seed):
+    """Ring attention (CP = 1) of Ulysses device `dev` over all n * s_local tokens
+    of its head slice, against the oracle on `rows`."""
+    xq, xk, xv = x3
+    y = [ra.ulysses_permute(to_device(x, "bf16"), n) for x in (xq, xk, xv)]
+    S = y[0].shape[1]
+    out, lse = _nan_outputs(S, H // n, d, torch.float32)
+    print(f"ulysses seed {seed} device {dev} rows {len(rows)}", flush=True)
+    ra.ra_forward(y[0][dev], y[1][dev:dev + 1], y[2][dev:dev + 1], None, 1, 0, "contiguous", out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    ri = torch.from_numpy(rows).cuda()
+    o, l = out[ri].cpu().numpy(), lse[:, ri].cpu().numpy()
+    del y, out, lse
+    # oracle: device `dev` holds every token of heads [dev H/n, (dev+1) H/n); under the
+    # causal mask no row sees a key past the sampled maximum, so the oracle is given
+    # keys [0, max(rows)] only (the others contribute exactly nothing)
+    kmax = int(rows.max()) + 1
+    gq = synth.bf16_bits_to_f64(oracle.ulysses_permute(xq, n)[dev])
+    gk = synth.bf16_bits_to_f64(oracle.ulysses_permute(xk, n)[dev][:kmax])
+    gv = synth.bf16_bits_to_f64(oracle.ulysses_permute(xv, n)[dev][:kmax])
+    O, L = oracle.attention_rows(gq[rows], rows, gk, gv, np.arange(kmax), None, S)
+    eo, el = max_abs(o, O), max_abs(l, L)
+    assert eo <= TOL_O_BF16 and el <= TOL_LSE_BF16, f"device {dev}: max-abs O {eo:.3e} LSE {el:.3e}"
+
+
+@pytest.mark.parametrize("seed,devices", [(0, ((0, 2048), (3, 256))), (1, ((2, 256),))])
+def test_ulysses_path_sampled(seed, devices):
     """[S/N=32768, H=32, d=128] x 4 simulated ranks permuted to [131072, 8, 128],
-    causal attention over 131072 tokens for rank 0's 8 heads, inverse permute."""
+    causal attention over 131072 tokens for a device's 8 heads, inverse permute.
+    Rows include the boundaries between the source ranks' chunks (multiples of 32768)."""
     n, sl, H, d = 4, 32768, 32, 128
-    xq = synth.make_ulysses_inputs(n, sl, H, d, seed=0, tid=synth.TID_Q)
-    xk = synth.make_ulysses_inputs(n, sl, H, d, seed=0, tid=synth.TID_K)
-    xv = synth.make_ulysses_inputs(n, sl, H, d, seed=0, tid=synth.TID_V)
-    yq = ra.ulysses_permute(to_device(xq, "bf16"), n)
-    yk = ra.ulysses_permute(to_device(xk, "bf16"), n)
-    yv = ra.ulysses_permute(to_device(xv, "bf16"), n)
     S = n * sl
-    out, lse = ra.ra_forward(yq[0], yk[0:1], yv[0:1], None, 1, 0, "contiguous", out_dtype=torch.float32)
-    o_all = torch.zeros((n, S, H // n, d), dtype=torch.bfloat16, device="cuda")
-    ra.ra_forward(yq[0], yk[0:1], yv[0:1], None, 1, 0, "contiguous", out=o_all[0])
+    x3 = [synth.make_ulysses_inputs(n, sl, H, d, seed=seed, tid=t) for t in (synth.TID_Q, synth.TID_K, synth.TID_V)]
+    for dev, n_rows in devices:
+        bounds = [b + o for b in (sl, 2 * sl, 3 * sl) for o in (-2, -1, 0, 1)] + [S - 1]
+        rows = sample_rows(S, extra=bounds, n_random=n_rows, seed=100 * seed + dev)
+        _ulysses_device_check(x3, n, H, d, dev, rows, seed)
+    if seed != 0:
+        return
+    # bf16 output into the full [4, 131072, 8, 128] buffer, then the inverse permute, bit-exact
+    xq, xk, xv = x3
+    yq, yk, yv = (ra.ulysses_permute(to_device(x, "bf16"), n) for x in x3)
+    o_all = torch.full((n, S, H // n, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for dev in range(n):
+        ra.ra_forward(yq[dev], yk[dev:dev + 1], yv[dev:dev + 1], None, 1, 0, "contiguous", out=o_all[dev])
     back = ra.ulysses_permute(o_all, n, inverse=True)
     torch.cuda.synchronize()
-    # oracle: device 0 holds every token of heads 0..7
-    gq = synth.bf16_bits_to_f64(oracle.ulysses_permute(xq, n)[0])
-    gk = synth.bf16_bits_to_f64(oracle.ulysses_permute(xk, n)[0])
-    gv = synth.bf16_bits_to_f64(oracle.ulysses_permute(xv, n)[0])
-    rows = sample_rows(S, extra=(sl - 1, sl, 2 * sl, 3 * sl - 1), n_random=16)
-    O, L = oracle.attention_rank(gq, gk, gv, None, 1, 0, "contiguous", rows=rows)
-    ri = torch.from_numpy(rows).cuda()
-    assert max_abs(out[ri].cpu().numpy(), O) <= TOL_O_BF16
-    assert max_abs(lse[:, ri].cpu().numpy(), L) <= TOL_LSE_BF16
-    # the inverse permute returns device 0's heads to the sequence-split layout, bit-exactly
+    assert bool(torch.isfinite(o_all.float()).all())
     exp_back = oracle.ulysses_permute(device_bits(o_all), n, inverse=True)
     assert np.array_equal(device_bits(back), exp_back)
     assert np.array_equal(device_bits(back)[:, :, : H // n], device_bits(o_all[0]).reshape(n, sl, H // n, d))
