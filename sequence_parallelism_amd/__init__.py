@@ -281,8 +281,11 @@ def ra_forward(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partit
                causal: bool = True, softmax_scale: float = 0.0, out_dtype=None, out=None, lse=None,
                workspace=None, stream=None, s_total=None):
     """One rank's ring attention. q [S_l,hq,d]; k, v [cp,S_l,hkv,d] (rank-major chunks).
+    The output dtype is out_dtype, else out's dtype when out is given, else q's.
     Returns (out [S_l,hq,d], lse fp32 [hq,S_l])."""
     import torch
+    if out_dtype is None and out is not None:
+        out_dtype = out.dtype
     shape, s_l, hq, d, out_dtype = _attn_common(q, k, v, cp_size, causal, softmax_scale, out_dtype, partition,
                                                 cu_seqlens, s_total)
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
@@ -638,7 +641,8 @@ def usp_forward(q, k, v, cu_seqlens=None, ulysses: int = 1, ring: int = 1, parti
     _need(q, "q", q.shape)
     _need(k, "k", k.shape, q.dtype)
     _need(v, "v", k.shape, q.dtype)
-    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else q.dtype
     S = R * U * sh
     shape = make_shape(S, hq, hkv, d, causal, softmax_scale, _dtype_code(q.dtype), _dtype_code(out_dtype))
     cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)

@@ -26,7 +26,10 @@ def test_forward_checks_every_tensor():
     q, k, v = _qkv()
     f = ra.ra_forward
     _raises("out must have shape", f, q, k, v, None, 4, 0, "zigzag", out=torch.zeros((255, 4, 64), dtype=BF))
-    _raises("out must be", f, q, k, v, None, 4, 0, "zigzag", out=torch.zeros((256, 4, 64), dtype=F32))
+    _raises("out must be", f, q, k, v, None, 4, 0, "zigzag", out=torch.zeros((256, 4, 64), dtype=F32),
+            out_dtype=BF)
+    # without out_dtype, a given out sets it (fp32 here): the call gets past the dtype check
+    _raises("on a GPU", f, q, k, v, None, 4, 0, "zigzag", out=torch.zeros((256, 4, 64), dtype=F32))
     _raises("lse must have shape", f, q, k, v, None, 4, 0, "zigzag", lse=torch.zeros((256, 4), dtype=F32))
     _raises("lse must be", f, q, k, v, None, 4, 0, "zigzag", lse=torch.zeros((4, 256), dtype=BF))
     _raises("k has shape", f, q, k[:3], v[:3], None, 4, 0, "zigzag")
