@@ -47,9 +47,10 @@
  *     keys; a row with no visible key has O = 0, LSE = -inf.
  *   - GQA: query head h reads KV head h / (hq / hkv).
  *   - All device pointers are caller-owned (e.g. PyTorch tensors). The library
- *     never allocates or frees device memory and keeps no global state; the
- *     caller supplies scratch space as `workspace` (size from
- *     ra_workspace_size). All calls are asynchronous on `stream` (a
+ *     never allocates or frees device memory; the caller supplies scratch space
+ *     as `workspace` (size from ra_workspace_size). The one exception is
+ *     ra_forward_noalloc, whose plan lives in a fixed array of device memory
+ *     that the library holds on each GPU (its only global state). All calls are asynchronous on `stream` (a
  *     hipStream_t; NULL = the default stream). Host arrays (cu_seqlens) are
  *     read before the call returns and may be freed right after.
  *   - Errors are return codes. Arguments are validated on the host before
@@ -76,7 +77,8 @@ typedef enum {
   RA_ERR_RANK = 6,          /* rank outside [0, cp_size)                                   */
   RA_ERR_UNSUPPORTED = 7,   /* head_dim / dtype / element size combination not provided    */
   RA_ERR_WORKSPACE = 8,     /* workspace NULL or smaller than ra_workspace_size()          */
-  RA_ERR_HIP = 9            /* a HIP launch or copy failed                                 */
+  RA_ERR_HIP = 9,           /* a HIP launch or copy failed                                 */
+  RA_ERR_SCRATCH = 10       /* ra_forward_noalloc: the plan exceeds RA_NOALLOC_SCRATCH_BYTES */
 } ra_status;
 
 /* How the global sequence is split over CP ranks (rank r, S_l = S / cp):
@@ -150,6 +152,25 @@ ra_status ra_forward(const void* q, const void* k, const void* v, const int32_t*
                      int32_t n_docs, int32_t cp_size, int32_t rank, int32_t partition,
                      const ra_shape* shape, void* out, float* lse, void* workspace, size_t ws_bytes,
                      void* stream);
+
+/* Bytes of fixed device scratch that ra_forward_noalloc can use (16 MiB). The plan
+ * of a share takes about cp * S_l^2 / 4096 bytes (S_l = tokens per rank), e.g.
+ * 4 MiB for 131072 tokens on one rank, 0.5 MiB for 8 ranks of 16384. */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* ra_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same arguments,
+ * results and errors as ra_forward, without the workspace: the plan lives in a
+ * fixed array of RA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * has run this call on, until the process ends. The call allocates and frees
+ * nothing. Arguments whose plan needs more than RA_NOALLOC_SCRATCH_BYTES (at most
+ * ra_workspace_size() bytes) give RA_ERR_SCRATCH before anything is launched.
+ * `stream` must belong to the current device. Every call on one GPU uses that
+ * GPU's array and leaves its plan there: calls that overlap in time on one GPU
+ * (other streams, other host threads) race, so the caller orders them. */
+ra_status ra_forward_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             int32_t n_docs, int32_t cp_size, int32_t rank, int32_t partition,
+                             const ra_shape* shape, void* out, float* lse, void* stream);
 
 /* Planning half of ra_forward (not for RA_PART_DOC_ZIGZAG, whose local length
  * ra_forward_planned could not know): uploads cu_seqlens and builds, in `workspace`,

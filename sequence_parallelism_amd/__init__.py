@@ -4,7 +4,7 @@ Argument marshalling only: every step of the path runs in the HIP kernels of
 libra.so. PyTorch provides device memory and the current stream. The binding
 fails loudly when the library is missing; there is no fallback of any kind.
 
-Function names mirror the C entry points: ra_forward, ra_plan,
+Function names mirror the C entry points: ra_forward, ra_forward_noalloc, ra_plan,
 ra_forward_planned, ra_forward_steps, ra_backward, ra_lse_merge, ra_classify,
 ulysses_permute, ulysses_permute_strided, usp_forward, cp_reorder,
 cp_reorder_docs, ra_local_length, ra_workspace_size, ra_backward_workspace_size,
@@ -25,11 +25,13 @@ LIB_PATH = os.path.join(_HERE, "libra.so")
 RA_OK = 0
 RA_ERR_NULL, RA_ERR_SHAPE, RA_ERR_DIVISIBILITY, RA_ERR_HEADS = 1, 2, 3, 4
 RA_ERR_CU_SEQLENS, RA_ERR_RANK, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE, RA_ERR_HIP = 5, 6, 7, 8, 9
+RA_ERR_SCRATCH = 10
+NOALLOC_SCRATCH_BYTES = 16 << 20  # RA_NOALLOC_SCRATCH_BYTES of include/ra.h
 RA_BF16, RA_F32 = 0, 1
 PARTITIONS = {"contiguous": 0, "zigzag": 1, "striped": 2, "doc_zigzag": 3}
 
 # Symbols declared in include/ra.h.
-EXPORTS = ("ra_workspace_size", "ra_forward", "ra_plan", "ra_forward_planned", "ra_forward_steps",
+EXPORTS = ("ra_workspace_size", "ra_forward", "ra_forward_noalloc", "ra_plan", "ra_forward_planned", "ra_forward_steps",
            "ra_backward_workspace_size", "ra_backward", "ra_lse_merge", "ra_classify",
            "ulysses_permute", "ulysses_permute_strided", "usp_workspace_size", "usp_forward",
            "cp_reorder", "cp_reorder_docs", "ra_local_length", "ra_doc_workspace_size",
@@ -66,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_workspace_size.restype = sz
     lib.ra_forward.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
     lib.ra_forward.restype = ctypes.c_int
+    lib.ra_forward_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp]
+    lib.ra_forward_noalloc.restype = ctypes.c_int
     lib.ra_plan.argtypes = [shp, vp, i32, i32, i32, i32, vp, sz, vp]
     lib.ra_plan.restype = ctypes.c_int
     lib.ra_forward_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
@@ -306,6 +310,28 @@ def ra_forward(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partit
                                            _part(partition), ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(ws),
                                            ws_bytes, st)
     _check(status, "ra_forward")
+    return out, lse
+
+
+def ra_forward_noalloc(q, k, v, cu_seqlens=None, cp_size: int = 1, rank: int = 0, partition="contiguous", *,
+                       out, lse, causal: bool = True, softmax_scale: float = 0.0, stream=None, s_total=None):
+    """ra_forward without any allocation, for callers that cannot allocate: the
+    caller passes out [S_l,hq,d] and lse fp32 [hq,S_l]; the plan lives in the
+    library's fixed per-GPU scratch (NOALLOC_SCRATCH_BYTES). Calls that overlap on
+    one GPU race. Returns (out, lse)."""
+    import torch
+    if out is None or lse is None:
+        raise ValueError("ra_forward_noalloc allocates nothing: pass out and lse")
+    shape, s_l, hq, d, out_dtype = _attn_common(q, k, v, cp_size, causal, softmax_scale, out.dtype, partition,
+                                                cu_seqlens, s_total)
+    cu_arr, n_docs, cu_ptr = _cu_array(cu_seqlens)
+    _need(out, "out", (s_l, hq, d), out_dtype)
+    _need(lse, "lse", (hq, s_l), torch.float32)
+    _same_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))
+    st = _torch_stream(stream).cuda_stream
+    status = load_library().ra_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), cu_ptr, n_docs, int(cp_size), int(rank),
+                                               _part(partition), ctypes.byref(shape), _ptr(out), _ptr(lse), st)
+    _check(status, "ra_forward_noalloc")
     return out, lse
 
 

@@ -3,6 +3,7 @@
 // then enqueues its kernels on the caller's stream.
 #include <math.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/ra.h"
@@ -190,6 +191,33 @@ ra_status run_backward(const void* q, const void* k, const void* v, const void* 
   return launch_ring_bwd(a, shape->d, shape->in_dtype == RA_BF16, st) == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Fixed scratch of ra_forward_noalloc. Every GPU the library runs on holds its own
+// copy of this array until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: the array's address on a device comes
+// from hipGetSymbolAddress with that device current, taken once per device and
+// kept in scratch_ptr[]; only that address is ever passed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[RA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up on the first call on that
+// device), or nullptr if the runtime reports an error.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -208,6 +236,7 @@ const char* ra_status_string(ra_status s) {
     case RA_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, element size or partition";
     case RA_ERR_WORKSPACE: return "workspace missing or smaller than ra_workspace_size()";
     case RA_ERR_HIP: return "HIP launch failed";
+    case RA_ERR_SCRATCH: return "the plan needs more than RA_NOALLOC_SCRATCH_BYTES of fixed scratch";
   }
   return "unknown status";
 }
@@ -235,6 +264,26 @@ ra_status ra_forward(const void* q, const void* k, const void* v, const int32_t*
   if (p != RA_OK) return p;
   return run_attention(q, k, v, layout_for(shape, cp_size, partition, cu_seqlens, nd), nd, cp_size, rank, partition,
                        shape, out, lse, nullptr, nullptr, workspace, st, false);
+}
+
+ra_status ra_forward_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                             int32_t n_docs, int32_t cp_size, int32_t rank, int32_t partition,
+                             const ra_shape* shape, void* out, float* lse, void* stream) {
+  // every check of ra_forward except the workspace's, which the fixed scratch replaces
+  const ra_status s = check_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, partition, shape, out, lse,
+                                    (const void*)out, SIZE_MAX);
+  if (s != RA_OK) return s;
+  const int32_t nd = effective_docs(cu_seqlens, n_docs);
+  const Layout L = layout_for(shape, cp_size, partition, cu_seqlens, nd);
+  if (L.total > RA_NOALLOC_SCRATCH_BYTES) return RA_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (!ws) return RA_ERR_HIP;
+  const hipStream_t st = as_stream(stream);
+  // the plan writes every scratch entry that the attention kernel reads (counts,
+  // order and the first count entries of each list): nothing needs clearing
+  const ra_status p = run_plan(L, cu_seqlens, nd, cp_size, rank, partition, shape, ws, st);
+  if (p != RA_OK) return p;
+  return run_attention(q, k, v, L, nd, cp_size, rank, partition, shape, out, lse, nullptr, nullptr, ws, st, false);
 }
 
 ra_status ra_plan(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size, int32_t rank,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         assert ra.ra_status_string(code) != "unknown status"
     assert ra.ra_status_string(99) == "unknown status"
 
@@ -247,6 +247,26 @@ def test_doc_zigzag_validation_and_lengths():
     assert lib.cp_reorder_docs(P, P2, 512, 2, 128, 2, 4, arr, 4, 0, P, 64, None) == ra.RA_ERR_WORKSPACE
     # the forward's workspace size covers the doc-zigzag layout
     assert fwd(sh, cu=cu, n_docs=4, part=3, ws_bytes=ra.ra_workspace_size(sh, 4, 4) - 1, q=None) == ra.RA_ERR_NULL
+
+
+def test_noalloc_validation_codes():
+    lib = _lib()
+    sh = shape()
+
+    def na(sh, q=P, out=P, cp=4, rank=0, part=1):
+        return lib.ra_forward_noalloc(q, P, P, None, 0, cp, rank, part, ctypes.byref(sh), out, P, None)
+
+    assert na(sh, q=None) == ra.RA_ERR_NULL
+    assert na(sh, out=None) == ra.RA_ERR_NULL
+    assert na(sh, rank=4) == ra.RA_ERR_RANK
+    assert na(shape(d=96)) == ra.RA_ERR_UNSUPPORTED
+    assert na(shape(s_total=4 * 1001)) == ra.RA_ERR_DIVISIBILITY
+    # 2^20 tokens on one rank: a 256 MiB plan, above the fixed scratch (refused before any launch)
+    assert na(shape(s_total=1 << 20, hq=1, hkv=1, d=64), cp=1, part=0) == ra.RA_ERR_SCRATCH
+    # the largest workload shapes fit: 131072 tokens on one rank, 8 x 16384 under doc-zigzag bounds
+    big = shape(s_total=131072, hq=8, hkv=8, d=128)
+    assert ra.ra_workspace_size(big, 1, 0) <= ra.NOALLOC_SCRATCH_BYTES
+    assert ra.ra_workspace_size(shape(s_total=131072), 8, 32) <= ra.NOALLOC_SCRATCH_BYTES
 
 
 def test_probe_validation_codes():
