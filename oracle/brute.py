@@ -14,22 +14,41 @@ from __future__ import annotations
 import math
 
 
-def brute_positions(partition, S, cp, r, cu=None, align=64):
+def brute_piece_bound(L, n, k, g):
+    """The multiple of g nearest to k*L/n (the larger one on a tie), at most L:
+    candidates compared in integers, |m*g*n - k*L|."""
+    if k == n:
+        return L
+    best = None
+    for m in range(L // g + 2):
+        dist = abs(m * g * n - k * L)
+        if best is None or dist <= best[0]:
+            best = (dist, m)
+    return min(L, best[1] * g)
+
+
+def brute_positions(partition, S, cp, r, cu=None, g=256):
     """Positions of rank r in local order; None marks doc_zigzag padding."""
     out = []
     sl = S // cp
     if partition == "doc_zigzag":
         bounds = cu if cu is not None else [0, S]
         n = 2 * cp
-        for j in range(len(bounds) - 1):
-            L = bounds[j + 1] - bounds[j]
-            sizes = [L // n + (1 if k < L % n else 0) for k in range(n)]
-            slots = align * ((max(sizes) + align - 1) // align)
-            for k in (r, n - 1 - r):
-                first = bounds[j] + sum(sizes[:k])
-                for i in range(slots):
-                    out.append(first + i if i < sizes[k] else None)
-        return out
+        ranks = []
+        for rr in range(cp):
+            mine = []
+            for j in range(len(bounds) - 1):
+                L = bounds[j + 1] - bounds[j]
+                pair = (rr + j) % cp
+                for k in (pair, n - 1 - pair):
+                    lo, hi = brute_piece_bound(L, n, k, g), brute_piece_bound(L, n, k + 1, g)
+                    piece = [bounds[j] + t for t in range(lo, hi)]
+                    while len(piece) % g:
+                        piece.append(None)
+                    mine.extend(piece)
+            ranks.append(mine)
+        width = max(len(x) for x in ranks)
+        return ranks[r] + [None] * (width - len(ranks[r]))
     if partition == "contiguous":
         for i in range(sl):
             out.append(r * sl + i)

@@ -17,14 +17,21 @@ positions(): which global token positions a CP rank holds, in its local order.
                 that ring-flash-attention adds balancing and variable-length
                 handling), and [LongCtx]'s timeline names dynamic CP for it,
                 without a layout. Reading: every document j (length L_j, from
-                cu_seqlens) is cut into 2*CP contiguous pieces of floor(L_j/2CP)
-                or one more tokens (the first L_j mod 2CP pieces get the extra
-                one), each padded at its end to P_j = A * ceil(ceil(L_j/2CP)/A)
-                slots, A = 64; rank r holds, document after document, piece r
-                and then piece 2*CP-1-r. Padding slots have position -1: they
-                see nothing and nothing sees them. Every rank holds sum_j 2 P_j
-                slots, and every document's causal work splits evenly, as zigzag
-                does for one sequence.
+                cu_seqlens) is cut into 2*CP contiguous pieces at the bounds
+                b_k = min(L_j, G * round(k * L_j / (2*CP*G))), k = 0..2*CP
+                (halves rounded up, b_{2CP} = L_j), G = 256 tokens: the zigzag
+                cut of the document with every inner bound moved to the
+                nearest multiple of G. Piece pair p of document j is piece p
+                and piece 2*CP-1-p; rank r holds pair p = (r + j) mod CP,
+                document after document, piece p first, each non-empty piece
+                padded at its end to a multiple of G slots (only a document's
+                last non-empty piece is ever short of one). Every rank's slots
+                are then padded at the end to S_l, the largest rank's count.
+                Padding slots have position -1: they see nothing and nothing
+                sees them. Pairs are the zigzag's balanced halves; rotating
+                them by document spreads the rounding and the padded last
+                pieces over the ranks, and bounds on multiples of G keep
+                whole query tiles of G rows inside one document.
 
 Documents: cu_seqlens [n_docs+1] are packed-document offsets ([XTuner-09]
 section 9.5): tokens of different documents must not attend to each other.
@@ -38,28 +45,42 @@ from __future__ import annotations
 import numpy as np
 
 
-PIECE_ALIGN = 64  # doc_zigzag pieces are padded to a multiple of this many tokens
+DOC_GRANULE = 256  # doc_zigzag piece bounds fall on multiples of this many tokens
 
 
-def doc_zigzag_piece_lengths(cu_seqlens, s_total: int, cp: int, align: int = PIECE_ALIGN) -> np.ndarray:
-    """Padded piece length P_j (slots) of every document under doc_zigzag."""
-    cu = np.asarray([0, s_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
-    L = cu[1:] - cu[:-1]
-    longest = -(-L // (2 * cp))
-    return align * (-(-longest // align))
-
-
-def doc_zigzag_piece_bounds(L: int, cp: int) -> np.ndarray:
-    """Document-relative start of each of the 2*CP pieces, plus the end [2*CP+1]."""
+def doc_zigzag_piece_bounds(L: int, cp: int, g: int = DOC_GRANULE) -> np.ndarray:
+    """Document-relative bounds b_0..b_{2CP} of the 2*CP pieces of a document of
+    length L: k*L/(2CP) rounded to the nearest multiple of g (halves up), capped
+    at L, and b_{2CP} = L."""
     n = 2 * cp
     k = np.arange(n + 1, dtype=np.int64)
-    return k * (L // n) + np.minimum(k, L % n)
+    b = g * ((2 * k * L + n * g) // (2 * n * g))  # g * floor(k L / (n g) + 1/2)
+    b = np.minimum(b, L)
+    b[n] = L
+    return b
+
+
+def doc_zigzag_rank_runs(cu_seqlens, s_total: int, cp: int, rank: int, g: int = DOC_GRANULE):
+    """Runs (first position, tokens, slots) of `rank` in local order, before the
+    end padding: for every document, piece p = (rank + j) mod CP and then piece
+    2*CP-1-p, empty pieces left out, each padded to a multiple of g slots."""
+    cu = np.asarray([0, s_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    runs = []
+    for j in range(len(cu) - 1):
+        b = doc_zigzag_piece_bounds(int(cu[j + 1] - cu[j]), cp, g)
+        p = (rank + j) % cp
+        for piece in (p, 2 * cp - 1 - p):
+            n_tok = int(b[piece + 1] - b[piece])
+            if n_tok > 0:
+                runs.append((int(cu[j] + b[piece]), n_tok, g * -(-n_tok // g)))
+    return runs
 
 
 def local_length(partition: str, s_total: int, cp: int, cu_seqlens=None) -> int:
-    """Tokens each rank holds (padding included for doc_zigzag)."""
+    """Tokens each rank holds (padding included for doc_zigzag: the largest
+    rank's slot count)."""
     if partition == "doc_zigzag":
-        return int(2 * doc_zigzag_piece_lengths(cu_seqlens, s_total, cp).sum())
+        return max(sum(s for _, _, s in doc_zigzag_rank_runs(cu_seqlens, s_total, cp, r)) for r in range(cp))
     return s_total // cp
 
 
@@ -67,15 +88,12 @@ def positions(partition: str, s_total: int, cp: int, rank: int, cu_seqlens=None)
     """Global positions held by `rank`, in its local order (int64 [S_l]; -1 marks
     doc_zigzag padding)."""
     if partition == "doc_zigzag":
-        cu = np.asarray([0, s_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
-        P = doc_zigzag_piece_lengths(cu, s_total, cp)
-        out = []
-        for j in range(len(cu) - 1):
-            b = doc_zigzag_piece_bounds(int(cu[j + 1] - cu[j]), cp)
-            for piece in (rank, 2 * cp - 1 - rank):
-                i = np.arange(P[j], dtype=np.int64)
-                out.append(np.where(i < b[piece + 1] - b[piece], cu[j] + b[piece] + i, -1))
-        return np.concatenate(out) if out else np.zeros(0, dtype=np.int64)
+        out = np.full(local_length("doc_zigzag", s_total, cp, cu_seqlens), -1, dtype=np.int64)
+        at = 0
+        for first, n_tok, slots in doc_zigzag_rank_runs(cu_seqlens, s_total, cp, rank):
+            out[at:at + n_tok] = np.arange(first, first + n_tok)
+            at += slots
+        return out
     if partition == "contiguous":
         if s_total % cp:
             raise ValueError("S must be divisible by CP")
