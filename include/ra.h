@@ -89,18 +89,21 @@ typedef enum {
  *                       ([LongCtx] timeline, Striped Attention)
  *   RA_PART_DOC_ZIGZAG  per-document zigzag for packed documents ([How-to] 2:
  *                       variable lengths magnify Ring's imbalance; [LongCtx]
- *                       timeline, dynamic CP): every document (cu_seqlens; NULL
- *                       = one document) is cut into 2 cp contiguous pieces of
- *                       floor(L/2cp) or one more tokens (the first L mod 2cp
- *                       pieces get the extra one), each padded at its end to
- *                       64 ceil(ceil(L/2cp)/64) slots; rank r holds, document
- *                       after document, piece r then piece 2 cp - 1 - r. Padding
- *                       slots see nothing and are seen by nothing (their O = 0,
- *                       LSE = -inf, gradients 0). S_l is then ra_local_length()
- *                       (> S / cp); S need not divide by cp. Accepted by
- *                       ra_forward, ra_forward_steps, ra_backward and ra_classify
- *                       (tiles 16, 32, 64 or 128); cp_reorder_docs moves data in
- *                       and out of this layout.                              */
+ *                       timeline, dynamic CP): every document j (cu_seqlens;
+ *                       NULL = one document, length L) is cut into 2 cp pieces
+ *                       at the bounds k L / 2cp rounded to the nearest multiple
+ *                       of 256 tokens (halves up, capped at L; the last bound
+ *                       is L). Rank r holds, document after document, piece
+ *                       p = (r + j) mod cp then piece 2 cp - 1 - p, each
+ *                       non-empty piece padded at its end to whole multiples
+ *                       of 256 slots, then padding up to S_l, the largest
+ *                       rank's slot count. Padding slots see nothing and are
+ *                       seen by nothing (their O = 0, LSE = -inf, gradients
+ *                       0). S_l = ra_local_length() (a multiple of 256); S need
+ *                       not divide by cp. Accepted by ra_forward,
+ *                       ra_forward_steps, ra_backward and ra_classify (tiles
+ *                       16, 32, 64 or 128); cp_reorder_docs moves data in and
+ *                       out of this layout.                                   */
 typedef enum {
   RA_PART_CONTIGUOUS = 0,
   RA_PART_ZIGZAG = 1,
@@ -127,8 +130,8 @@ typedef struct {
  * for every partition. Returns 0 for an invalid shape. */
 size_t ra_workspace_size(const ra_shape* shape, int32_t cp_size, int32_t n_docs);
 
-/* Tokens (slots) one rank holds: S / cp, or for RA_PART_DOC_ZIGZAG the padded
- * per-document pieces. cu_seqlens is a HOST array (NULL: one document). Returns
+/* Tokens (slots) one rank holds: S / cp, or for RA_PART_DOC_ZIGZAG the largest
+ * rank's padded pieces. cu_seqlens is a HOST array (NULL: one document). Returns
  * -1 for invalid arguments (including S not divisible as the partition needs). */
 int64_t ra_local_length(int64_t s_total, int32_t cp_size, int32_t partition, const int32_t* cu_seqlens,
                         int32_t n_docs);

@@ -21,7 +21,7 @@ inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Compact doc-zigzag tables (ra_classify, cp_reorder_docs): cu, block prefix, descriptors.
+// Compact doc-zigzag tables (ra_classify, cp_reorder_docs): cu, per-rank block prefix, descriptors.
 struct DocRegions {
   size_t cu_off, prefix_off, blk_off, total;
   int nblk;
@@ -31,7 +31,7 @@ DocRegions doc_regions(int32_t nd, int32_t cp, int64_t s_local) {
   DocRegions R{};
   R.cu_off = 0;
   R.prefix_off = round256((size_t)(nd + 1) * 4);
-  R.blk_off = R.prefix_off + round256((size_t)(nd + 1) * 4);
+  R.blk_off = R.prefix_off + round256((size_t)cp * (nd + 1) * 4);
   R.nblk = (int)(s_local / 64);
   R.total = R.blk_off + (size_t)cp * R.nblk * 8;
   return R;
@@ -39,36 +39,28 @@ DocRegions doc_regions(int32_t nd, int32_t cp, int64_t s_local) {
 
 ra_status upload_doc_tables(char* ws, const DocRegions& R, const ra_shape* shape, const int32_t* cu, int32_t nd,
                             int32_t cp, hipStream_t st) {
-  std::vector<int32_t> one{0, (int32_t)shape->s_total}, prefix((size_t)nd + 1);
-  const int32_t* hcu = cu ? cu : one.data();
-  local_len(shape, cp, RA_PART_DOC_ZIGZAG, cu, nd, prefix.data());
+  const int32_t one[2] = {0, (int32_t)shape->s_total};
   int* dcu = (int*)(ws + R.cu_off);
-  if (launch_upload_i32(hcu, nd + 1, dcu, st) != hipSuccess ||
-      launch_upload_i32(prefix.data(), nd + 1, (int*)(ws + R.prefix_off), st) != hipSuccess ||
-      launch_doc_blocks(dcu, (const int*)(ws + R.prefix_off), nd, cp, R.nblk, (int2*)(ws + R.blk_off), st) !=
-          hipSuccess)
+  if (launch_upload_i32(cu ? cu : one, nd + 1, dcu, st) != hipSuccess ||
+      launch_doc_blocks(dcu, (int*)(ws + R.prefix_off), nd, cp, R.nblk, (int2*)(ws + R.blk_off), st) != hipSuccess)
     return RA_ERR_HIP;
   return RA_OK;
 }
 
 // Layout of the attention workspace for validated arguments (host cu_seqlens, or NULL).
 Layout layout_for(const ra_shape* shape, int32_t cp, int32_t partition, const int32_t* cu, int32_t nd) {
-  return attn_layout(shape, cp, nd, partition, local_len(shape, cp, partition, cu, nd, nullptr));
+  return attn_layout(shape, cp, nd, partition, local_len(shape, cp, partition, cu, nd));
 }
 
-// Uploads cu_seqlens (and, for doc-zigzag, the block prefix, then builds the block
-// descriptors); the device pointers land in the layout's regions of `workspace`.
+// Uploads cu_seqlens (and, for doc-zigzag, builds the per-rank block prefix and the
+// block descriptors); the device pointers land in the layout's regions of `workspace`.
 ra_status upload_docs(const Layout& L, const int32_t* cu, int32_t nd, int32_t cp, int32_t partition,
                       const ra_shape* shape, char* ws, hipStream_t st) {
   int* dcu = (int*)(ws + L.cu_off);
   if (L.doczig) {
-    std::vector<int32_t> one{0, (int32_t)shape->s_total}, prefix((size_t)nd + 1);
-    const int32_t* hcu = cu ? cu : one.data();
-    local_len(shape, cp, partition, cu, nd, prefix.data());
-    if (launch_upload_i32(hcu, nd + 1, dcu, st) != hipSuccess ||
-        launch_upload_i32(prefix.data(), nd + 1, (int*)(ws + L.prefix_off), st) != hipSuccess ||
-        launch_doc_blocks(dcu, (const int*)(ws + L.prefix_off), nd, cp, L.nblk, (int2*)(ws + L.blk_off), st) !=
-            hipSuccess)
+    const int32_t one[2] = {0, (int32_t)shape->s_total};
+    if (launch_upload_i32(cu ? cu : one, nd + 1, dcu, st) != hipSuccess ||
+        launch_doc_blocks(dcu, (int*)(ws + L.prefix_off), nd, cp, L.nblk, (int2*)(ws + L.blk_off), st) != hipSuccess)
       return RA_ERR_HIP;
   } else if (nd > 1 && launch_upload_i32(cu, nd + 1, dcu, st) != hipSuccess) {
     return RA_ERR_HIP;
@@ -137,7 +129,7 @@ ra_status run_attention(const void* q, const void* k, const void* v, const Layou
 ra_status run_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
                        const void* dout, const int32_t* cu, int32_t nd, int32_t cp, int32_t rank, int32_t partition,
                        const ra_shape* shape, float* dq, float* dk, float* dv, void* workspace, hipStream_t st) {
-  const BwdLayout B = bwd_layout(shape, cp, nd, partition, local_len(shape, cp, partition, cu, nd, nullptr));
+  const BwdLayout B = bwd_layout(shape, cp, nd, partition, local_len(shape, cp, partition, cu, nd));
   const Layout& L = B.fwd;
   char* ws = (char*)workspace;
   const ra_status p = run_plan(L, cu, nd, cp, rank, partition, shape, workspace, st);
@@ -360,7 +352,7 @@ ra_status ra_classify(const ra_shape* shape, const int32_t* cu_seqlens, int32_t 
   if (s != RA_OK) return s;
   const hipStream_t st = as_stream(stream);
   const int32_t nd = effective_docs(cu_seqlens, n_docs);
-  const int s_local = (int)local_len(shape, cp_size, partition, cu_seqlens, nd, nullptr);
+  const int s_local = (int)local_len(shape, cp_size, partition, cu_seqlens, nd);
   int* dcu = nd > 1 ? (int*)workspace : nullptr;
   const int2* blk = nullptr;
   if (partition == RA_PART_DOC_ZIGZAG) {
@@ -471,7 +463,7 @@ int64_t ra_local_length(int64_t s_total, int32_t cp_size, int32_t partition, con
     const int64_t div = partition == RA_PART_ZIGZAG ? 2 * (int64_t)cp_size : cp_size;
     return s_total % div == 0 ? s_total / cp_size : -1;
   }
-  return local_len(&shp, cp_size, partition, cu_seqlens, effective_docs(cu_seqlens, n_docs), nullptr);
+  return local_len(&shp, cp_size, partition, cu_seqlens, effective_docs(cu_seqlens, n_docs));
 }
 
 size_t ra_doc_workspace_size(int64_t s_total, int32_t cp_size, const int32_t* cu_seqlens, int32_t n_docs) {
@@ -490,14 +482,13 @@ ra_status cp_reorder_docs(const void* in, void* out, int64_t s, int32_t h, int32
   const int32_t nd = effective_docs(cu_seqlens, n_docs);
   ra_shape shp{};
   shp.s_total = s;
-  const int64_t sl = local_len(&shp, cp_size, RA_PART_DOC_ZIGZAG, cu_seqlens, nd, nullptr);
+  const int64_t sl = local_len(&shp, cp_size, RA_PART_DOC_ZIGZAG, cu_seqlens, nd);
   const DocRegions R = doc_regions(nd, cp_size, sl);
   char* ws = (char*)workspace;
   const ra_status u = upload_doc_tables(ws, R, &shp, cu_seqlens, nd, cp_size, st);
   if (u != RA_OK) return u;
-  return launch_cp_reorder_docs(in, out, s, (int64_t)h * d * elem_bytes, cp_size, (int)sl,
-                                (const int*)(ws + R.cu_off), (const int*)(ws + R.prefix_off),
-                                (const int2*)(ws + R.blk_off), nd, inverse, st) == hipSuccess
+  return launch_cp_reorder_docs(in, out, (int64_t)h * d * elem_bytes, cp_size, (int)sl,
+                                (const int2*)(ws + R.blk_off), inverse, st) == hipSuccess
              ? RA_OK
              : RA_ERR_HIP;
 }

@@ -129,37 +129,91 @@ hipError_t launch_order(const int* count, int n, int* order, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Doc-zigzag block descriptors. Rank r's local slots are, document after
-// document, piece r then piece 2cp-1-r of that document, each piece padded to
-// half = (prefix[j+1] - prefix[j]) / 2 blocks. Pieces hold floor(L/2cp) or one
-// more tokens (the first L mod 2cp pieces the extra one), real tokens first.
+// Doc-zigzag block descriptors. Document j (length L) is cut into 2cp pieces at
+// the bounds k L / 2cp rounded to the nearest multiple of kDocGranule (halves
+// up, capped at L); rank r holds, document after document, piece p = (r + j)
+// mod cp and then piece 2cp-1-p, each padded to whole granules, real tokens
+// first. prefix[r][j] counts the 64-slot blocks rank r holds before document j.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ long long doc_bound(long long L, int cp, int k) {
+  const long long n = 2 * cp;
+  if (k >= n) return L;
+  const long long b = kDocGranule * ((2 * k * L + n * kDocGranule) / (2 * n * kDocGranule));
+  return b < L ? b : L;
+}
+
+__device__ __forceinline__ int granule_blocks(long long len) {
+  return (int)((len + kDocGranule - 1) / kDocGranule) * (kDocGranule / kDocBlock);
+}
+
+// One workgroup per rank: blocks of every document, scanned in chunks of 256.
+__global__ void __launch_bounds__(256) doc_prefix_kernel(const int* cu, int n_docs, int cp, int* prefix) {
+  __shared__ int part[256];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  int* pr = prefix + (size_t)r * (n_docs + 1);
+  if (tid == 0) pr[0] = 0;
+  int carry = 0;
+  for (int j0 = 0; j0 < n_docs; j0 += 256) {
+    const int j = j0 + tid;
+    int nb = 0;
+    if (j < n_docs) {
+      const long long L = cu[j + 1] - cu[j];
+      const int p = (int)((r + (long long)j) % cp), q = 2 * cp - 1 - p;
+      nb = granule_blocks(doc_bound(L, cp, p + 1) - doc_bound(L, cp, p)) +
+           granule_blocks(doc_bound(L, cp, q + 1) - doc_bound(L, cp, q));
+    }
+    part[tid] = nb;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive scan (Hillis-Steele)
+      const int add = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    if (j < n_docs) pr[j + 1] = carry + part[tid];
+    carry += part[255];
+    __syncthreads();
+  }
+}
+
+// One thread per (rank, block): the document by binary search in the rank's
+// prefix, then the piece and the block's offset in it.
 __global__ void __launch_bounds__(256) doc_blocks_kernel(const int* cu, const int* prefix, int n_docs, int cp,
                                                          int nblk, int2* blk) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= cp * nblk) return;
   const int r = idx / nblk, b = idx - r * nblk;
-  int lo = 0, hi = n_docs - 1;  // document: largest j with prefix[j] <= b
+  const int* pr = prefix + (size_t)r * (n_docs + 1);
+  if (b >= pr[n_docs]) {  // the rank's end padding
+    blk[idx] = make_int2(0, 0);
+    return;
+  }
+  int lo = 0, hi = n_docs - 1;  // document: smallest j with pr[j + 1] > b
   while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= b) lo = mid; else hi = mid - 1;
+    const int mid = (lo + hi) >> 1;
+    if (pr[mid + 1] > b) hi = mid; else lo = mid + 1;
   }
   const int j = lo;
-  const int half = (prefix[j + 1] - prefix[j]) >> 1;
-  const int lb = b - prefix[j];
-  const int piece = lb < half ? r : 2 * cp - 1 - r;
-  const int bip = lb < half ? lb : lb - half;
-  const int L = cu[j + 1] - cu[j], n = 2 * cp;
-  const int q = L / n, rem = L % n;
-  const int pstart = piece * q + (piece < rem ? piece : rem);
-  const int psize = q + (piece < rem ? 1 : 0);
-  int cnt = psize - bip * kDocBlock;
+  const long long L = cu[j + 1] - cu[j];
+  const int p = (int)((r + (long long)j) % cp), q = 2 * cp - 1 - p;
+  const long long p0 = doc_bound(L, cp, p), p1 = doc_bound(L, cp, p + 1);
+  const int first_blocks = granule_blocks(p1 - p0);
+  int lb = b - pr[j];
+  long long start = p0, len = p1 - p0;
+  if (lb >= first_blocks) {
+    lb -= first_blocks;
+    start = doc_bound(L, cp, q);
+    len = doc_bound(L, cp, q + 1) - start;
+  }
+  long long cnt = len - (long long)lb * kDocBlock;
   cnt = cnt < 0 ? 0 : (cnt > kDocBlock ? kDocBlock : cnt);
-  blk[idx] = make_int2(cu[j] + pstart + bip * kDocBlock, cnt);
+  blk[idx] = make_int2(cu[j] + (int)start + lb * kDocBlock, (int)cnt);
 }
 
-hipError_t launch_doc_blocks(const int* cu, const int* prefix, int n_docs, int cp, int nblk, int2* blk,
-                             hipStream_t st) {
+hipError_t launch_doc_blocks(const int* cu, int* prefix, int n_docs, int cp, int nblk, int2* blk, hipStream_t st) {
+  hipLaunchKernelGGL(doc_prefix_kernel, dim3(cp), dim3(256), 0, st, cu, n_docs, cp, prefix);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const long long n = (long long)cp * nblk;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(doc_blocks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cu, prefix, n_docs, cp,
@@ -167,48 +221,24 @@ hipError_t launch_doc_blocks(const int* cu, const int* prefix, int n_docs, int c
   return hipGetLastError();
 }
 
-// Doc-zigzag reorder, one wave per destination row. Forward: row R = (rank, slot)
-// takes global row pos(rank, slot), or zeros for padding. Inverse: global row p
-// takes the slot that holds it (document j by binary search in cu, piece and
-// offset from the piece sizes).
+// Doc-zigzag reorder, one wave per row of the rank-major layout R = (rank, slot),
+// whose global row comes from the block descriptors. Forward: row R takes that
+// global row, or zeros for padding. Inverse: the global row takes row R (every
+// real token is held by exactly one slot, so every output row is written once).
 struct DocCopyArgs {
   const void* in;
   void* out;
-  long long nrows;   // destination rows
+  long long nrows;   // rank-major rows: cp * s_local
   long long cpr;     // chunks per row
-  int s_local, cp, n_docs;
-  const int* cu;
-  const int* prefix;
+  int s_local;
   const int2* blk;
 };
 
-__device__ __forceinline__ long long doc_src_row(const DocCopyArgs& c, long long R, bool inverse) {
-  if (!inverse) {
-    const int r = (int)(R / c.s_local), i = (int)(R - (long long)r * c.s_local);
-    const int2 b = c.blk[r * (c.s_local / kDocBlock) + i / kDocBlock];
-    const int o = i % kDocBlock;
-    return o < b.y ? (long long)(b.x + o) : -1;
-  }
-  const int p = (int)R;
-  int lo = 0, hi = c.n_docs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (c.cu[mid] <= p) lo = mid; else hi = mid - 1;
-  }
-  const int j = lo, rel = p - c.cu[j];
-  const int L = c.cu[j + 1] - c.cu[j], n = 2 * c.cp, q = L / n, rem = L % n;
-  int k, off;
-  if (rel < rem * (q + 1)) {
-    k = rel / (q + 1);
-    off = rel - k * (q + 1);
-  } else {
-    k = rem + (rel - rem * (q + 1)) / q;
-    off = rel - rem * (q + 1) - (k - rem) * q;
-  }
-  const int half = (c.prefix[j + 1] - c.prefix[j]) >> 1;
-  const int r = k < c.cp ? k : n - 1 - k;
-  const int i = c.prefix[j] * kDocBlock + (k < c.cp ? 0 : half * kDocBlock) + off;
-  return (long long)r * c.s_local + i;
+__device__ __forceinline__ long long doc_global_row(const DocCopyArgs& c, long long R) {
+  const int r = (int)(R / c.s_local), i = (int)(R - (long long)r * c.s_local);
+  const int2 b = c.blk[r * (c.s_local / kDocBlock) + i / kDocBlock];
+  const int o = i % kDocBlock;
+  return o < b.y ? (long long)(b.x + o) : -1;
 }
 
 template <typename T, bool INVERSE>
@@ -216,13 +246,14 @@ __global__ void __launch_bounds__(256) copy_doc_rows_kernel(const DocCopyArgs c)
   const int lane = threadIdx.x & 63;
   const long long nw = (long long)gridDim.x * 4;
   for (long long R = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); R < c.nrows; R += nw) {
-    const long long S = doc_src_row(c, R, INVERSE);
-    T* dst = (T*)c.out + R * c.cpr;
-    if (S < 0) {
+    const long long G = doc_global_row(c, R);
+    if (INVERSE && G < 0) continue;  // padding slot: nothing to put back
+    T* dst = (T*)c.out + (INVERSE ? G : R) * c.cpr;
+    if (G < 0) {
       for (long long i = lane; i < c.cpr; i += 64) dst[i] = T{};
       continue;
     }
-    const T* src = (const T*)c.in + S * c.cpr;
+    const T* src = (const T*)c.in + (INVERSE ? R : G) * c.cpr;
     long long i = lane;
     for (; i + 192 < c.cpr; i += 256) {
       const T a0 = src[i], a1 = src[i + 64], a2 = src[i + 128], a3 = src[i + 192];
@@ -255,16 +286,10 @@ static hipError_t launch_doc_copy(DocCopyArgs c, long long row_bytes, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_cp_reorder_docs(const void* in, void* out, int64_t s, int64_t row_bytes, int cp, int s_local,
-                                  const int* cu, const int* prefix, const int2* blk, int n_docs, int inverse,
-                                  hipStream_t st) {
-  DocCopyArgs c{in, out, 0, 0, s_local, cp, n_docs, cu, prefix, blk};
-  if (inverse) {
-    c.nrows = s;
-    return launch_doc_copy<true>(c, row_bytes, st);
-  }
-  c.nrows = (long long)cp * s_local;
-  return launch_doc_copy<false>(c, row_bytes, st);
+hipError_t launch_cp_reorder_docs(const void* in, void* out, int64_t row_bytes, int cp, int s_local, const int2* blk,
+                                  int inverse, hipStream_t st) {
+  DocCopyArgs c{in, out, (long long)cp * s_local, 0, s_local, blk};
+  return inverse ? launch_doc_copy<true>(c, row_bytes, st) : launch_doc_copy<false>(c, row_bytes, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -28,8 +28,9 @@ namespace ra {
 
 enum { PART_CONTIGUOUS = 0, PART_ZIGZAG = 1, PART_STRIPED = 2, PART_DOC_ZIGZAG = 3 };
 
-// Slots per doc-zigzag block (pieces are padded to a multiple of this).
+// Slots per doc-zigzag block (each block holds one run of positions, then padding).
 constexpr int kDocBlock = 64;
+constexpr int kDocGranule = 256;  // doc-zigzag piece bounds fall on multiples of this many tokens
 enum { CLS_SKIP = 0, CLS_PARTIAL = 1, CLS_FULL = 2 };
 
 // Work-list entry: bits 0-1 class, bits 2-7 ring step, bits 8-31 key tile.

@@ -31,12 +31,27 @@ ra_status check_divisible(int64_t s, int32_t cp, int32_t partition) {
   return s % cp == 0 ? RA_OK : RA_ERR_DIVISIBILITY;
 }
 
-constexpr int64_t kDocBlock = 64;  // doc-zigzag block (must match the device code)
+constexpr int64_t kDocBlock = 64;     // doc-zigzag block (must match the device code)
+constexpr int64_t kDocGranule = 256;  // doc-zigzag piece bound granule (must match the device code)
 
-// Blocks per rank of one document of length L under doc-zigzag.
-int64_t doc_blocks(int64_t L, int32_t cp) {
-  const int64_t longest = (L + 2 * cp - 1) / (2 * cp);
-  return 2 * ((longest + kDocBlock - 1) / kDocBlock);
+// Document-relative bound k (0..2cp) of the doc-zigzag pieces of a document of
+// length L: k L / 2cp rounded to the nearest multiple of the granule (halves
+// up), capped at L; bound 2cp is L.
+int64_t doc_bound(int64_t L, int32_t cp, int64_t k) {
+  const int64_t n = 2 * (int64_t)cp;
+  if (k >= n) return L;
+  const int64_t b = kDocGranule * ((2 * k * L + n * kDocGranule) / (2 * n * kDocGranule));
+  return b < L ? b : L;
+}
+
+// 64-slot blocks that rank r holds of document j (length L): piece pair
+// p = (r + j) mod cp, i.e. pieces p and 2cp-1-p, each padded to whole granules.
+int64_t doc_rank_blocks(int64_t L, int32_t cp, int32_t r, int32_t j) {
+  const int64_t p = (r + (int64_t)j) % cp, q = 2 * (int64_t)cp - 1 - p;
+  const int64_t a = doc_bound(L, cp, p + 1) - doc_bound(L, cp, p);
+  const int64_t b = doc_bound(L, cp, q + 1) - doc_bound(L, cp, q);
+  const int64_t g = kDocGranule / kDocBlock;
+  return g * ((a + kDocGranule - 1) / kDocGranule + (b + kDocGranule - 1) / kDocGranule);
 }
 
 bool overlaps(const void* a, const void* b, uint64_t bytes) {
@@ -80,26 +95,29 @@ ra_status check_cu(const int32_t* cu, int32_t n_docs, int64_t s_total) {
 
 int32_t effective_docs(const int32_t* cu, int32_t n_docs) { return cu ? n_docs : 1; }
 
-int64_t local_len(const ra_shape* shape, int32_t cp_size, int32_t partition, const int32_t* cu, int32_t n_docs,
-                  int32_t* prefix) {
+int64_t local_len(const ra_shape* shape, int32_t cp_size, int32_t partition, const int32_t* cu, int32_t n_docs) {
   if (partition != RA_PART_DOC_ZIGZAG) return shape->s_total / cp_size;
   const int32_t nd = cu ? n_docs : 1;
-  int64_t blocks = 0;
-  if (prefix) prefix[0] = 0;
-  for (int32_t j = 0; j < nd; ++j) {
-    const int64_t L = cu ? (int64_t)cu[j + 1] - cu[j] : shape->s_total;
-    blocks += doc_blocks(L, cp_size);
-    if (blocks * kDocBlock > ((int64_t)1 << 31) - 1) return -1;
-    if (prefix) prefix[j + 1] = (int32_t)blocks;
+  int64_t widest = 0;
+  for (int32_t r = 0; r < cp_size; ++r) {
+    int64_t blocks = 0;
+    for (int32_t j = 0; j < nd; ++j) {
+      const int64_t L = cu ? (int64_t)cu[j + 1] - cu[j] : shape->s_total;
+      blocks += doc_rank_blocks(L, cp_size, r, j);
+      if (blocks * kDocBlock > ((int64_t)1 << 31) - 1) return -1;
+    }
+    widest = blocks > widest ? blocks : widest;
   }
-  return blocks * kDocBlock;
+  return widest * kDocBlock;
 }
 
 int64_t local_len_bound(const ra_shape* shape, int32_t cp_size, int32_t n_docs) {
-  // each document adds at most 2 * 64 slots of rounding over its share L / cp
+  // a piece exceeds L / 2cp by at most one granule (each bound moves by at most
+  // half a granule), and only a document's last piece is padded (by less than a
+  // granule): a rank holds at most L / cp + 3 granules of slots per document
   const int64_t nd = n_docs > 1 ? n_docs : 1;
   const int64_t base = (shape->s_total + cp_size - 1) / cp_size;
-  return ((base + 2 * kDocBlock * nd + 2 + kDocBlock - 1) / kDocBlock) * kDocBlock;
+  return ((base + 3 * kDocGranule * nd + kDocGranule - 1) / kDocGranule) * kDocGranule;
 }
 
 Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, int32_t partition, int64_t s_local,
@@ -118,7 +136,7 @@ Layout attn_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev, i
   const size_t cu_bytes = (L.n_docs_dev > 1 || L.doczig) ? (size_t)(L.n_docs_dev + 1) * 4 : 0;
   L.cu_off = 0;
   L.prefix_off = align256(L.cu_off + cu_bytes);
-  L.blk_off = align256(L.prefix_off + (L.doczig ? (size_t)(L.n_docs_dev + 1) * 4 : 0));
+  L.blk_off = align256(L.prefix_off + (L.doczig ? (size_t)cp_size * (L.n_docs_dev + 1) * 4 : 0));
   L.count_off = align256(L.blk_off + (L.doczig ? (size_t)cp_size * L.nblk * 8 : 0));
   L.order_off = align256(L.count_off + (size_t)L.nqt * 4);
   L.wl_off = align256(L.order_off + (size_t)L.nqt * 4);
@@ -151,7 +169,7 @@ BwdLayout bwd_layout(const ra_shape* shape, int32_t cp_size, int32_t n_docs_dev,
 // and one chunk at `elem` bytes per element (doc-zigzag lengths exceed S / cp).
 ra_status checked_local_len(const ra_shape* shape, int32_t cp_size, int32_t partition, const int32_t* cu,
                             int32_t n_docs, int64_t elem, int64_t& s_local) {
-  s_local = local_len(shape, cp_size, partition, cu, n_docs, nullptr);
+  s_local = local_len(shape, cp_size, partition, cu, n_docs);
   if (s_local < 1) return RA_ERR_SHAPE;
   const int64_t heads = shape->hq > shape->hkv ? shape->hq : shape->hkv;
   if (s_local * heads * shape->d * elem > 0x7fffffffLL) return RA_ERR_SHAPE;
@@ -224,10 +242,11 @@ ra_status check_forward_planned(const void* q, const void* k, const void* v, int
   return RA_OK;
 }
 
-// Compact doc-zigzag tables of ra_classify / cp_reorder_docs: cu and block prefix
-// (256-byte aligned), then the block descriptors.
+// Compact doc-zigzag tables of ra_classify / cp_reorder_docs: cu, the per-rank
+// block prefix (each 256-byte aligned), then the block descriptors.
 size_t classify_doc_ws(int32_t nd, int32_t cp_size, int64_t s_local) {
-  return align256((size_t)(nd + 1) * 4) * 2 + (size_t)cp_size * (size_t)(s_local / kDocBlock) * 8;
+  return align256((size_t)(nd + 1) * 4) + align256((size_t)cp_size * (nd + 1) * 4) +
+         (size_t)cp_size * (size_t)(s_local / kDocBlock) * 8;
 }
 
 ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_docs, int32_t cp_size, int32_t rank,
@@ -250,7 +269,7 @@ ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_doc
     // tiles must not span more than two 64-slot blocks
     const auto pow2_le128 = [](int32_t x) { return x == 16 || x == 32 || x == 64 || x == 128; };
     if (!pow2_le128(bm) || !pow2_le128(bn)) return RA_ERR_UNSUPPORTED;
-    const int64_t sl = local_len(shape, cp_size, partition, cu, n_docs, nullptr);
+    const int64_t sl = local_len(shape, cp_size, partition, cu, n_docs);
     if (sl < 1) return RA_ERR_SHAPE;
     need = classify_doc_ws(nd, cp_size, sl);
   }
@@ -367,7 +386,7 @@ ra_status check_cp_reorder_docs(const void* in, const void* out, int64_t s, int3
   if (st != RA_OK) return st;
   ra_shape shp{};
   shp.s_total = s;
-  const int64_t sl = local_len(&shp, cp_size, RA_PART_DOC_ZIGZAG, cu, n_docs, nullptr);
+  const int64_t sl = local_len(&shp, cp_size, RA_PART_DOC_ZIGZAG, cu, n_docs);
   if (sl < 1) return RA_ERR_SHAPE;
   const uint64_t row = (uint64_t)h * (uint64_t)d * (uint64_t)elem_bytes;
   const uint64_t in_bytes = inverse ? (uint64_t)cp_size * sl * row : (uint64_t)s * row;

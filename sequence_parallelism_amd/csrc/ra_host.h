@@ -20,10 +20,8 @@ struct Layout {
 };
 
 // Tokens (slots) each rank holds: s_total / cp, or for RA_PART_DOC_ZIGZAG the
-// padded per-document pieces (cu NULL: one document). Also fills the per-document
-// block prefix [n_docs + 1] when `prefix` is non-NULL. Returns -1 on overflow.
-int64_t local_len(const ra_shape* shape, int32_t cp_size, int32_t partition, const int32_t* cu, int32_t n_docs,
-                  int32_t* prefix);
+// largest rank's padded pieces (cu NULL: one document). Returns -1 on overflow.
+int64_t local_len(const ra_shape* shape, int32_t cp_size, int32_t partition, const int32_t* cu, int32_t n_docs);
 
 // Upper bound of local_len over every cu_seqlens with n_docs documents.
 int64_t local_len_bound(const ra_shape* shape, int32_t cp_size, int32_t n_docs);

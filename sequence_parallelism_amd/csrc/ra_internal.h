@@ -36,16 +36,15 @@ hipError_t launch_worklist(const int* cu, const int2* blk, int n_docs, int s_tot
                            int part, int causal, int bm, int bn, int nqt, int nkt, int wl_stride, int* wl,
                            int* wl_count, int* order, hipStream_t st);
 
-// Doc-zigzag block descriptors [cp][nblk] from device cu_seqlens [n_docs+1] and the
-// per-document block prefix [n_docs+1] (blocks per rank before document j).
-hipError_t launch_doc_blocks(const int* cu, const int* prefix, int n_docs, int cp, int nblk, int2* blk,
-                             hipStream_t st);
+// Doc-zigzag block descriptors [cp][nblk] from device cu_seqlens [n_docs+1]; the
+// per-rank block prefix [cp][n_docs+1] (blocks rank r holds before document j) is
+// written to `prefix` on the way.
+hipError_t launch_doc_blocks(const int* cu, int* prefix, int n_docs, int cp, int nblk, int2* blk, hipStream_t st);
 
-// Doc-zigzag CP reorder: forward [s][row] -> [cp][s_local][row] (padding rows zero);
-// inverse [cp][s_local][row] -> [s][row].
-hipError_t launch_cp_reorder_docs(const void* in, void* out, int64_t s, int64_t row_bytes, int cp, int s_local,
-                                  const int* cu, const int* prefix, const int2* blk, int n_docs, int inverse,
-                                  hipStream_t st);
+// Doc-zigzag CP reorder through the block descriptors: forward [s][row] ->
+// [cp][s_local][row] (padding rows zero); inverse [cp][s_local][row] -> [s][row].
+hipError_t launch_cp_reorder_docs(const void* in, void* out, int64_t row_bytes, int cp, int s_local, const int2* blk,
+                                  int inverse, hipStream_t st);
 
 // Orders n tiles by descending count (ties by index) into order[0..n).
 hipError_t launch_order(const int* count, int n, int* order, hipStream_t st);

@@ -5,9 +5,12 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import sequence_parallelism_amd as ra
+import synth
+from oracle.partition import local_length as oracle_local_length
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 P = ctypes.c_void_p(0x100000)           # stand-in device pointer: never dereferenced by validation
@@ -222,11 +225,15 @@ def test_doc_zigzag_validation_and_lengths():
     lib = _lib()
     cu = [0, 100, 101, 333, 512]
     arr = (ctypes.c_int32 * len(cu))(*cu)
-    # local length: every document in 2cp pieces of ceil(L/2cp) padded to 64 slots, 2 pieces per rank
-    assert ra.ra_local_length(512, 4, "doc_zigzag", cu) == 64 * 2 * 4
+    # local length: the largest rank's pieces, each padded to whole 256-slot granules
+    for S, cp, c in ((512, 4, cu), (510, 4, None), (131072, 8, None), (2600, 3, [0, 1000, 1001, 2600]),
+                     (131072, 8, list(synth.loguniform_cu_seqlens(0, 131072, 512, 32768)))):
+        assert ra.ra_local_length(S, cp, "doc_zigzag", c) == oracle_local_length(
+            "doc_zigzag", S, cp, None if c is None else np.asarray(c)), (S, cp)
     assert ra.ra_local_length(512, 4, "zigzag", cu) == 128
     assert ra.ra_local_length(510, 4, "zigzag") == -1          # not divisible by 2cp
-    assert ra.ra_local_length(510, 4, "doc_zigzag") == 128     # one padded document: 2 * 64
+    assert ra.ra_local_length(510, 4, "doc_zigzag") == 256     # pieces [0, 256) and [256, 510) on two ranks
+    assert ra.ra_local_length(131072, 8, "doc_zigzag") == 16384  # one document: the zigzag split
     assert ra.ra_local_length(512, 4, "doc_zigzag", [0, 600, 512]) == -1
     assert ra.ra_doc_workspace_size(512, 4, cu) > 0
     # plans and the planned kernel, and the Ulysses x Ring grid, do not take doc-zigzag
