@@ -183,7 +183,7 @@ def main():
                          "1 GiB device copy (counter calibration); mfma-only: the register-only MFMA loop; "
                          "bwd-only: the backward of the Llama-2-7B-shaped share")
     ap.add_argument("--workload", default="ulysses", choices=["ulysses", "llama7b", "gqa", "packed", "packed_doc"])
-    ap.add_argument("--rank", type=int, default=None, help="attn-only: the rank (default: the headline rank)")
+    ap.add_argument("--rank", type=int, default=None, help="attn-only: the rank (default: the headline rank; -1: every rank in turn)")
     ap.add_argument("--which", default="ulysses_fwd",
                     choices=["ulysses_fwd", "ulysses_inv", "reorder_llama7b", "reorder_gqa_q", "reorder_gqa_kv",
                              "reorder_packed"])
@@ -374,19 +374,23 @@ def attn_only(np, torch, ra, synth, dev, workload, rank, launches):
         fl = 4.0 * U_D * hq * visible_pairs(np, "contiguous", S, 1, 0)
     else:
         w, part, cu, sl, q_all, k, v = _workload_tensors(np, torch, ra, synth, dev, workload, gen)
-        r = w.rank if rank is None else rank
-        if part == "doc_zigzag":
-            shape = ra.make_shape(w.s_total, w.hq, w.hkv, w.d, True, 0.0, ra.RA_BF16, ra.RA_BF16)
-            ws = torch.empty(ra.ra_workspace_size(shape, w.cp, len(cu) - 1), dtype=torch.uint8, device=dev)
-            for _ in range(launches):
-                ra.ra_forward(q_all[r], k, v, cu, w.cp, r, part, workspace=ws)
-            fl = 4.0 * w.d * w.hq * visible_pairs(np, "contiguous", w.s_total, 1, 0, cu) / w.cp
-        else:
-            plan = ra.ra_plan(w.s_total, w.hq, w.hkv, w.d, cu, w.cp, r, part)
-            out = torch.empty_like(q_all[r])
-            for _ in range(launches):
-                ra.ra_forward_planned(q_all[r], k, v, plan, out=out)
-            fl = 4.0 * w.d * w.hq * visible_pairs(np, part, w.s_total, w.cp, r, cu)
+        ranks = range(w.cp) if rank == -1 else [w.rank if rank is None else rank]  # -1: every rank in turn
+        fl = 0.0
+        for r in ranks:
+            if part == "doc_zigzag":
+                shape = ra.make_shape(w.s_total, w.hq, w.hkv, w.d, True, 0.0, ra.RA_BF16, ra.RA_BF16)
+                ws = torch.empty(ra.ra_workspace_size(shape, w.cp, len(cu) - 1), dtype=torch.uint8, device=dev)
+                for _ in range(launches):
+                    ra.ra_forward(q_all[r], k, v, cu, w.cp, r, part, workspace=ws)
+                # the ranks' shares of the documents' causal work are within a few percent
+                fl += 4.0 * w.d * w.hq * visible_pairs(np, "contiguous", w.s_total, 1, 0, cu) / w.cp
+            else:
+                plan = ra.ra_plan(w.s_total, w.hq, w.hkv, w.d, cu, w.cp, r, part)
+                out = torch.empty_like(q_all[r])
+                for _ in range(launches):
+                    ra.ra_forward_planned(q_all[r], k, v, plan, out=out)
+                fl += 4.0 * w.d * w.hq * visible_pairs(np, part, w.s_total, w.cp, r, cu)
+        fl /= len(ranks)
     torch.cuda.synchronize()
     print(json.dumps({"mode": "attn-only", "workload": workload, "rank": rank, "launches": launches,
                       "flops_per_launch": fl}), flush=True)
