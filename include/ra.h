@@ -175,12 +175,13 @@ ra_status ra_forward_noalloc(const void* q, const void* k, const void* v, const 
                              int32_t n_docs, int32_t cp_size, int32_t rank, int32_t partition,
                              const ra_shape* shape, void* out, float* lse, void* stream);
 
-/* Planning half of ra_forward (not for RA_PART_DOC_ZIGZAG, whose local length
- * ra_forward_planned could not know): uploads cu_seqlens and builds, in `workspace`,
- * the per-query-tile work list of non-SKIP (ring step, key tile) pairs with
- * their FULL / PARTIAL class ([CP-TE] 3.3) and the heaviest-first tile order.
+/* Planning half of ra_forward: uploads cu_seqlens (for RA_PART_DOC_ZIGZAG, also
+ * builds the block descriptors of the layout) and builds, in `workspace`, the
+ * per-query-tile work list of non-SKIP (ring step, key tile) pairs with their
+ * FULL / PARTIAL class ([CP-TE] 3.3) and the heaviest-first tile order.
  * A plan depends only on (shape, cu_seqlens, cp_size, rank, partition), so
- * one plan serves every layer that shares them. */
+ * one plan serves every layer that shares them. A RA_PART_DOC_ZIGZAG plan is
+ * executed by ra_forward_planned_docs, the others by ra_forward_planned. */
 ra_status ra_plan(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size,
                   int32_t rank, int32_t partition, void* workspace, size_t ws_bytes, void* stream);
 
@@ -192,6 +193,17 @@ ra_status ra_plan(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_do
 ra_status ra_forward_planned(const void* q, const void* k, const void* v, int32_t n_docs, int32_t cp_size,
                              int32_t rank, int32_t partition, const ra_shape* shape, void* out, float* lse,
                              void* workspace, size_t ws_bytes, void* stream);
+
+/* Execution half of ra_forward for RA_PART_DOC_ZIGZAG ([How-to] 2: packed
+ * documents of variable length): the attention kernel alone on the plan that
+ * ra_plan left in `workspace` for the same arguments. cu_seqlens is the HOST
+ * array the plan was made from; it sizes the local length S_l on the host and
+ * is not uploaded again. Arguments, layouts and errors as in ra_forward with
+ * partition RA_PART_DOC_ZIGZAG; a plan made for other arguments gives
+ * undefined values but no out-of-bounds access. */
+ra_status ra_forward_planned_docs(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                  int32_t n_docs, int32_t cp_size, int32_t rank, const ra_shape* shape, void* out,
+                                  float* lse, void* workspace, size_t ws_bytes, void* stream);
 
 /* Same inputs as ra_forward; writes each ring step's normalised partial instead
  * of the merged result:

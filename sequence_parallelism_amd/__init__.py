@@ -29,9 +29,11 @@ RA_ERR_SCRATCH = 10
 NOALLOC_SCRATCH_BYTES = 16 << 20  # RA_NOALLOC_SCRATCH_BYTES of include/ra.h
 RA_BF16, RA_F32 = 0, 1
 PARTITIONS = {"contiguous": 0, "zigzag": 1, "striped": 2, "doc_zigzag": 3}
+RA_PART_DOC_ZIGZAG = PARTITIONS["doc_zigzag"]
 
 # Symbols declared in include/ra.h.
-EXPORTS = ("ra_workspace_size", "ra_forward", "ra_forward_noalloc", "ra_plan", "ra_forward_planned", "ra_forward_steps",
+EXPORTS = ("ra_workspace_size", "ra_forward", "ra_forward_noalloc", "ra_plan", "ra_forward_planned",
+           "ra_forward_planned_docs", "ra_forward_steps",
            "ra_backward_workspace_size", "ra_backward", "ra_lse_merge", "ra_classify",
            "ulysses_permute", "ulysses_permute_strided", "usp_workspace_size", "usp_forward",
            "cp_reorder", "cp_reorder_docs", "ra_local_length", "ra_doc_workspace_size",
@@ -74,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ra_plan.restype = ctypes.c_int
     lib.ra_forward_planned.argtypes = [vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
     lib.ra_forward_planned.restype = ctypes.c_int
+    lib.ra_forward_planned_docs.argtypes = [vp, vp, vp, vp, i32, i32, i32, shp, vp, vp, vp, sz, vp]
+    lib.ra_forward_planned_docs.restype = ctypes.c_int
     lib.ra_forward_steps.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, shp, vp, vp, vp, sz, vp]
     lib.ra_forward_steps.restype = ctypes.c_int
     lib.ra_backward_workspace_size.argtypes = [shp, i32, i32]
@@ -349,11 +353,14 @@ def ra_probe_mfma(iters: int, workgroups: int, waves: int = 8, sink=None, stream
 
 
 class Plan:
-    """A work list built by ra_plan in a workspace tensor, for ra_forward_planned."""
+    """A work list built by ra_plan in a workspace tensor, for ra_forward_planned.
+    s_local is the rank's local length; cu (a host int32 array, or None) the
+    documents a per-document zigzag plan was made for."""
 
-    def __init__(self, shape, n_docs, cp_size, rank, partition, workspace, ws_bytes):
+    def __init__(self, shape, n_docs, cp_size, rank, partition, workspace, ws_bytes, s_local, cu=None):
         self.shape, self.n_docs, self.cp_size, self.rank = shape, n_docs, cp_size, rank
         self.partition, self.workspace, self.ws_bytes = partition, workspace, ws_bytes
+        self.s_local, self.cu = s_local, cu
 
 
 def ra_plan(s_total: int, hq: int, hkv: int, d: int, cu_seqlens=None, cp_size: int = 1, rank: int = 0,
@@ -376,17 +383,19 @@ def ra_plan(s_total: int, hq: int, hkv: int, d: int, cu_seqlens=None, cp_size: i
         status = load_library().ra_plan(ctypes.byref(shape), cu_ptr, n_docs, int(cp_size), int(rank),
                                         _part(partition), _ptr(ws), ws_bytes, st)
     _check(status, "ra_plan")
-    return Plan(shape, n_docs, int(cp_size), int(rank), _part(partition), ws, ws_bytes)
+    part = _part(partition)
+    s_l = ra_local_length(s_total, cp_size, partition, cu_seqlens)
+    return Plan(shape, n_docs, int(cp_size), int(rank), part, ws, ws_bytes, s_l,
+                cu_arr if part == RA_PART_DOC_ZIGZAG else None)
 
 
 def ra_forward_planned(q, k, v, plan: Plan, *, out=None, lse=None, stream=None):
     """The attention kernel alone, on a Plan from ra_plan. q, k, v (and out, lse when
-    given) must match the plan's shape: q [S/cp, hq, d], k, v [cp, S/cp, hkv, d]."""
+    given) must match the plan's shape: q [S_l, hq, d], k, v [cp, S_l, hkv, d] with
+    S_l = plan.s_local (S/cp, or the per-document zigzag length)."""
     import torch
     sh = plan.shape
-    if sh.s_total % plan.cp_size:
-        raise ValueError("plan: S not divisible by cp")
-    s_l = sh.s_total // plan.cp_size
+    s_l = plan.s_local
     in_dtype, out_dtype = _torch_dtype(sh.in_dtype), _torch_dtype(sh.out_dtype)
     _need(q, "q", (s_l, sh.hq, sh.d), in_dtype)
     _need(k, "k", (plan.cp_size, s_l, sh.hkv, sh.d), in_dtype)
@@ -401,9 +410,15 @@ def ra_forward_planned(q, k, v, plan: Plan, *, out=None, lse=None, stream=None):
             out = torch.empty((s_l, sh.hq, sh.d), dtype=out_dtype, device=dev)
         if lse is None:
             lse = torch.empty((sh.hq, s_l), dtype=torch.float32, device=dev)
-        status = load_library().ra_forward_planned(_ptr(q), _ptr(k), _ptr(v), plan.n_docs, plan.cp_size, plan.rank,
-                                                   plan.partition, ctypes.byref(sh), _ptr(out), _ptr(lse),
-                                                   _ptr(plan.workspace), plan.ws_bytes, st)
+        if plan.partition == RA_PART_DOC_ZIGZAG:
+            cu_ptr = plan.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if plan.cu is not None else None
+            status = load_library().ra_forward_planned_docs(_ptr(q), _ptr(k), _ptr(v), cu_ptr, plan.n_docs,
+                                                            plan.cp_size, plan.rank, ctypes.byref(sh), _ptr(out),
+                                                            _ptr(lse), _ptr(plan.workspace), plan.ws_bytes, st)
+        else:
+            status = load_library().ra_forward_planned(_ptr(q), _ptr(k), _ptr(v), plan.n_docs, plan.cp_size,
+                                                       plan.rank, plan.partition, ctypes.byref(sh), _ptr(out),
+                                                       _ptr(lse), _ptr(plan.workspace), plan.ws_bytes, st)
     _check(status, "ra_forward_planned")
     return out, lse
 

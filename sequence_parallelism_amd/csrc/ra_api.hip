@@ -214,7 +214,7 @@ void* device_scratch() {
 
 extern "C" {
 
-int32_t ra_abi_version(void) { return 2; }
+int32_t ra_abi_version(void) { return 3; }
 
 const char* ra_status_string(ra_status s) {
   switch (s) {
@@ -295,6 +295,17 @@ ra_status ra_forward_planned(const void* q, const void* k, const void* v, int32_
   const int32_t nd = n_docs > 1 ? n_docs : 1;
   return run_attention(q, k, v, attn_layout(shape, cp_size, nd, partition, shape->s_total / cp_size), nd, cp_size,
                        rank, partition, shape, out, lse, nullptr, nullptr, workspace, as_stream(stream), false);
+}
+
+ra_status ra_forward_planned_docs(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                                  int32_t n_docs, int32_t cp_size, int32_t rank, const ra_shape* shape, void* out,
+                                  float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  const ra_status s = check_forward(q, k, v, cu_seqlens, n_docs, cp_size, rank, RA_PART_DOC_ZIGZAG, shape, out, lse,
+                                    workspace, ws_bytes);
+  if (s != RA_OK) return s;
+  const int32_t nd = effective_docs(cu_seqlens, n_docs);
+  return run_attention(q, k, v, layout_for(shape, cp_size, RA_PART_DOC_ZIGZAG, cu_seqlens, nd), nd, cp_size, rank,
+                       RA_PART_DOC_ZIGZAG, shape, out, lse, nullptr, nullptr, workspace, as_stream(stream), false);
 }
 
 ra_status ra_forward_steps(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int32_t n_docs,

@@ -45,8 +45,11 @@ struct WlArgs {
   int* wl_count;
 };
 
-__global__ void __launch_bounds__(256) worklist_kernel(const WlArgs w) {
-  __shared__ int wave_tot[4];
+// 1024 threads per tile: each classification is a chain of dependent loads
+// (block descriptors, document bounds), so the more of them in flight the better.
+constexpr int kWlThreads = 1024, kWlWaves = kWlThreads / 64;
+__global__ void __launch_bounds__(kWlThreads) worklist_kernel(const WlArgs w) {
+  __shared__ int wave_tot[kWlWaves];
   const int I = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const PartInfo p{w.part, w.s_local, w.cp, w.blk};
@@ -55,7 +58,7 @@ __global__ void __launch_bounds__(256) worklist_kernel(const WlArgs w) {
   const int nent = w.cp * w.nkt;
   int* out = w.wl + (size_t)I * w.wl_stride;
   int base = 0;
-  for (int e0 = 0; e0 < nent; e0 += 256) {
+  for (int e0 = 0; e0 < nent; e0 += kWlThreads) {
     const int e = e0 + tid;
     int c = CLS_SKIP, t = 0, J = 0;
     if (e < nent) {
@@ -79,12 +82,15 @@ __global__ void __launch_bounds__(256) worklist_kernel(const WlArgs w) {
     const int below = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) wave_tot[wave] = __popcll(bal);
     __syncthreads();
-    int before = 0, total = 0;
+    // prefix over the waves' counts: lane i of every wave holds the sum of waves 0..i
+    int inc = lane < kWlWaves ? wave_tot[lane] : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      before += i < wave ? wave_tot[i] : 0;
-      total += wave_tot[i];
+    for (int o = 1; o < kWlWaves; o <<= 1) {
+      const int up = __shfl_up(inc, o, 64);
+      inc += lane >= o ? up : 0;
     }
+    const int total = __shfl(inc, kWlWaves - 1, 64);
+    const int before = wave > 0 ? __shfl(inc, wave - 1, 64) : 0;
     if (c != CLS_SKIP) out[base + before + below] = wl_pack(t, J, c);
     base += total;
     __syncthreads();
@@ -116,7 +122,7 @@ hipError_t launch_worklist(const int* cu, const int2* blk, int n_docs, int s_tot
                            int* wl_count, int* order, hipStream_t st) {
   if (nqt == 0) return hipSuccess;
   WlArgs w{cu, blk, n_docs, s_total, s_local, cp, rank, part, causal, bm, bn, nqt, nkt, wl_stride, wl, wl_count};
-  hipLaunchKernelGGL(worklist_kernel, dim3(nqt), dim3(256), 0, st, w);
+  hipLaunchKernelGGL(worklist_kernel, dim3(nqt), dim3(kWlThreads), 0, st, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_order(wl_count, nqt, order, st);

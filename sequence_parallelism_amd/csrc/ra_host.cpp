@@ -220,9 +220,10 @@ ra_status check_plan(const ra_shape* shape, const int32_t* cu, int32_t n_docs, i
   if (s != RA_OK) return s;
   s = check_cu(cu, n_docs, shape->s_total);
   if (s != RA_OK) return s;
-  // a plan serves ra_forward_planned, which takes no cu_seqlens to size a doc-zigzag share
-  if (partition == RA_PART_DOC_ZIGZAG) return RA_ERR_UNSUPPORTED;
-  const Layout L = attn_layout(shape, cp_size, effective_docs(cu, n_docs), partition, shape->s_total / cp_size);
+  int64_t sl;
+  s = checked_local_len(shape, cp_size, partition, cu, n_docs, shape->in_dtype == RA_BF16 ? 2 : 4, sl);
+  if (s != RA_OK) return s;
+  const Layout L = attn_layout(shape, cp_size, effective_docs(cu, n_docs), partition, sl);
   if ((int64_t)L.nqt * shape->hq > 0x7fffffffLL) return RA_ERR_SHAPE;
   if (!workspace || ws_bytes < L.total) return RA_ERR_WORKSPACE;
   return RA_OK;

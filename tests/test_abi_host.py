@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     assert names == set(ra.EXPORTS), names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.ra_abi_version() == 2
+    assert lib.ra_abi_version() == 3
 
 
 def test_status_strings():
@@ -236,11 +236,23 @@ def test_doc_zigzag_validation_and_lengths():
     assert ra.ra_local_length(131072, 8, "doc_zigzag") == 16384  # one document: the zigzag split
     assert ra.ra_local_length(512, 4, "doc_zigzag", [0, 600, 512]) == -1
     assert ra.ra_doc_workspace_size(512, 4, cu) > 0
-    # plans and the planned kernel, and the Ulysses x Ring grid, do not take doc-zigzag
+    # a doc-zigzag plan is sized by its documents and runs through ra_forward_planned_docs;
+    # ra_forward_planned (no cu_seqlens) and the Ulysses x Ring grid do not take doc-zigzag
     sh = shape(s_total=512, hq=2, hkv=2)
-    assert lib.ra_plan(ctypes.byref(sh), arr, 4, 4, 0, 3, P, 1 << 40, None) == ra.RA_ERR_UNSUPPORTED
+    need = ra.ra_workspace_size(sh, 4, 4)
+    assert lib.ra_plan(ctypes.byref(sh), arr, 4, 4, 0, 3, P, 64, None) == ra.RA_ERR_WORKSPACE
+    assert lib.ra_plan(ctypes.byref(sh), bad_cu := (ctypes.c_int32 * 3)(0, 600, 512), 2, 4, 0, 3, P, need, None) \
+        == ra.RA_ERR_CU_SEQLENS
     assert lib.ra_forward_planned(P, P, P, 4, 4, 0, 3, ctypes.byref(sh), P, P, P, 1 << 40, None) \
         == ra.RA_ERR_UNSUPPORTED
+    assert lib.ra_forward_planned_docs(None, P, P, arr, 4, 4, 0, ctypes.byref(sh), P, P, P, need, None) \
+        == ra.RA_ERR_NULL
+    assert lib.ra_forward_planned_docs(P, P, P, bad_cu, 2, 4, 0, ctypes.byref(sh), P, P, P, need, None) \
+        == ra.RA_ERR_CU_SEQLENS
+    assert lib.ra_forward_planned_docs(P, P, P, arr, 4, 4, 4, ctypes.byref(sh), P, P, P, need, None) \
+        == ra.RA_ERR_RANK
+    assert lib.ra_forward_planned_docs(P, P, P, arr, 4, 4, 0, ctypes.byref(sh), P, P, P, 64, None) \
+        == ra.RA_ERR_WORKSPACE
     assert lib.usp_forward(P, P, P, arr, 4, 2, 2, 3, ctypes.byref(sh), P, P, P, 1 << 40, None) \
         == ra.RA_ERR_UNSUPPORTED
     assert lib.cp_reorder(P, P2, 512, 2, 128, 2, 4, 3, 0, None) == ra.RA_ERR_UNSUPPORTED

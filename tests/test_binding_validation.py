@@ -55,7 +55,7 @@ def test_forward_doc_zigzag_checks_the_local_length():
 
 def test_planned_call_checks_tensors_against_the_plan():
     sh = ra.make_shape(1024, 4, 2, 64, True, 0.0, ra.RA_BF16, ra.RA_F32)
-    plan = ra.Plan(sh, 0, 4, 0, 1, torch.zeros(ra.ra_workspace_size(sh, 4, 0), dtype=torch.uint8), 0)
+    plan = ra.Plan(sh, 0, 4, 0, 1, torch.zeros(ra.ra_workspace_size(sh, 4, 0), dtype=torch.uint8), 0, 256)
     q, k, v = _qkv()
     f = ra.ra_forward_planned
     _raises("q must be", f, q.float(), k, v, plan)

@@ -88,6 +88,23 @@ def test_forward_bf16(cp, causal):
         _check(g, cp, rank, causal)
 
 
+@pytest.mark.parametrize("cp,d", [(4, 128), (3, 64)])
+def test_plan_then_planned_call_matches_ra_forward(cp, d):
+    """ra_plan + ra_forward_planned (the per-document zigzag entry point) gives
+    ra_forward's outputs bit for bit, on every rank and twice from one plan."""
+    g = _case(3000, 4, 2, d, "bf16", seed=40 + cp)
+    S = g.q.shape[0]
+    for rank in range(cp):
+        qr, kr, vr = rank_inputs(g, cp, rank, "doc_zigzag")
+        out, lse = ra.ra_forward(qr, kr, vr, g.cu_seqlens, cp, rank, "doc_zigzag", s_total=S)
+        plan = ra.ra_plan(S, 4, 2, d, g.cu_seqlens, cp, rank, "doc_zigzag")
+        assert plan.s_local == qr.shape[0]
+        for _ in range(2):
+            o2, l2 = ra.ra_forward_planned(qr, kr, vr, plan)
+            torch.cuda.synchronize()
+            assert torch.equal(o2, out) and torch.equal(l2, lse), f"rank {rank}"
+
+
 def test_forward_d64_bf16_output_and_fp32():
     g = _case(1500, 2, 2, 64, "bf16", seed=31)
     for rank in range(3):
