@@ -84,12 +84,16 @@ def visible_pairs(np, part, S, cp, r, cu=None, causal=True):
 # ---------------------------------------------------------------------------
 # Timing helpers (HIP events on the stream the library launches on)
 # ---------------------------------------------------------------------------
-def time_events(torch, fn, reps, warm=2):
+def time_events(torch, fn, reps, warm=2, flush=None):
+    """HIP-event times of `reps` calls of fn on the current stream (after `warm`
+    untimed ones); flush, when given, runs before each timed call, outside the events."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
     times = []
     for _ in range(reps):
+        if flush is not None:
+            flush()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -99,6 +103,29 @@ def time_events(torch, fn, reps, warm=2):
     torch.cuda.synchronize()
     ms = sorted(x.elapsed_time(y) for x, y in times)
     return {"avg_ms": sum(ms) / len(ms), "min_ms": ms[0], "median_ms": ms[len(ms) // 2]}
+
+
+_FLUSH = []
+
+
+def mall_flush(torch):
+    """Reads a 1 GiB scratch buffer, so that nothing of the previous repetition is
+    still in the 256 MB last-level cache (MALL) when the next one starts: its
+    inputs are gone, and its dirty output lines are written back during the flush
+    (a flush by writing would leave its own dirty lines to drain during the timed
+    kernel)."""
+    if not _FLUSH:
+        _FLUSH.append(torch.ones(1 << 28, dtype=torch.int32, device="cuda"))
+    _FLUSH[0].sum()
+
+
+def time_hbm(torch, fn, reps, nbytes):
+    """An HBM-bound kernel timed with the cache flushed before every repetition:
+    average, minimum and median, and GB/s at the average and at the minimum."""
+    t = time_events(torch, fn, reps, flush=lambda: mall_flush(torch))
+    return {"avg_ms": t["avg_ms"], "min_ms": t["min_ms"], "median_ms": t["median_ms"], "bytes": nbytes,
+            "gbs": gbs(nbytes, t["avg_ms"]), "gbs_best": gbs(nbytes, t["min_ms"]),
+            "frac_hbm_peak": gbs(nbytes, t["avg_ms"]) / PEAK_HBM_GBS}
 
 
 def traffic_from_profiles(kernel_src_sha):
@@ -280,14 +307,11 @@ def main():
         "avg_ms": attn["avg_ms"], "min_ms": attn["min_ms"], "median_ms": attn["median_ms"], "tflops": attn_tflops,
         "frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS, "flops": flops, "visible_pairs_per_head": pairs,
         "algorithmic_bytes": alg_bytes}}
-    t = time_events(torch, lambda: ra.ulysses_permute(xq, U_N, out=yq), args.steps)
     nbytes = 2 * xq.numel() * 2
-    kernels["ulysses_permute_n4_s32k_h32"] = {"avg_ms": t["avg_ms"], "bytes": nbytes, "gbs": gbs(nbytes, t["avg_ms"]),
-                                              "frac_hbm_peak": gbs(nbytes, t["avg_ms"]) / PEAK_HBM_GBS}
-    ti = time_events(torch, lambda: ra.ulysses_permute(o_all, U_N, inverse=True, out=back), args.steps)
-    kernels["ulysses_permute_inverse_n4_s128k_h8"] = {"avg_ms": ti["avg_ms"], "bytes": nbytes,
-                                                      "gbs": gbs(nbytes, ti["avg_ms"]),
-                                                      "frac_hbm_peak": gbs(nbytes, ti["avg_ms"]) / PEAK_HBM_GBS}
+    kernels["ulysses_permute_n4_s32k_h32"] = time_hbm(torch, lambda: ra.ulysses_permute(xq, U_N, out=yq),
+                                                      args.steps, nbytes)
+    kernels["ulysses_permute_inverse_n4_s128k_h8"] = time_hbm(
+        torch, lambda: ra.ulysses_permute(o_all, U_N, inverse=True, out=back), args.steps, nbytes)
     log(f"attention kernel {attn['avg_ms']:.3f} ms = {attn_tflops:.1f} TFLOP/s; Ulysses permute "
         f"{kernels['ulysses_permute_n4_s32k_h32']['gbs']:.0f} / inverse "
         f"{kernels['ulysses_permute_inverse_n4_s128k_h8']['gbs']:.0f} GB/s")
@@ -487,10 +511,9 @@ def extras(np, torch, ra, synth, dev, reps, reps_long):
     res["ring_attn_llama7b_zigzag_rank0"] = {"avg_ms": ta["avg_ms"], "min_ms": ta["min_ms"], "flops": fl,
                                              "tflops": fl / (ta["avg_ms"] * 1e-3) / 1e12,
                                              "frac_bf16_peak": fl / (ta["avg_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    tr = time_events(torch, lambda: ra.cp_reorder(k_g, cp, w.partition, out=k_p), reps)
     nbytes = 2 * k_g.numel() * 2
-    res["cp_reorder_s32k_h32_zigzag"] = {"avg_ms": tr["avg_ms"], "bytes": nbytes, "gbs": gbs(nbytes, tr["avg_ms"]),
-                                         "frac_hbm_peak": gbs(nbytes, tr["avg_ms"]) / PEAK_HBM_GBS}
+    res["cp_reorder_s32k_h32_zigzag"] = time_hbm(torch, lambda: ra.cp_reorder(k_g, cp, w.partition, out=k_p), reps,
+                                                 nbytes)
 
     # backward of the same share: dQ, and this rank's dK / dV partials of every chunk
     log("extras: backward of the zigzag share")
@@ -519,11 +542,9 @@ def extras(np, torch, ra, synth, dev, reps, reps_long):
     for h, tag in ((w.hq, "q"), (w.hkv, "kv")):
         x = _randn(torch, gen, dev, w.s_total, h, w.d)
         y = torch.empty((w.cp, slg, h, w.d), dtype=torch.bfloat16, device=dev)
-        t = time_events(torch, lambda: ra.cp_reorder(x, w.cp, w.partition, out=y), reps)
         nbytes = 2 * x.numel() * 2
-        res[f"cp_reorder_s64k_h{h}_striped_{tag}"] = {"avg_ms": t["avg_ms"], "bytes": nbytes,
-                                                      "gbs": gbs(nbytes, t["avg_ms"]),
-                                                      "frac_hbm_peak": gbs(nbytes, t["avg_ms"]) / PEAK_HBM_GBS}
+        res[f"cp_reorder_s64k_h{h}_striped_{tag}"] = time_hbm(
+            torch, lambda: ra.cp_reorder(x, w.cp, w.partition, out=y), reps, nbytes)
         del x, y
     del q, k, v
 
@@ -549,10 +570,9 @@ def extras(np, torch, ra, synth, dev, reps, reps_long):
                                            "tflops_all_ranks": total_fl / (sum_ms * 1e-3) / 1e12}
     x = _randn(torch, gen, dev, w.s_total, w.hq, w.d)
     y = torch.empty((w.cp, slp, w.hq, w.d), dtype=torch.bfloat16, device=dev)
-    t = time_events(torch, lambda: ra.cp_reorder(x, w.cp, w.partition, out=y), reps)
     nbytes = 2 * x.numel() * 2
-    res["cp_reorder_s128k_h32_zigzag"] = {"avg_ms": t["avg_ms"], "bytes": nbytes, "gbs": gbs(nbytes, t["avg_ms"]),
-                                          "frac_hbm_peak": gbs(nbytes, t["avg_ms"]) / PEAK_HBM_GBS}
+    res["cp_reorder_s128k_h32_zigzag"] = time_hbm(torch, lambda: ra.cp_reorder(x, w.cp, w.partition, out=y), reps,
+                                                  nbytes)
     del q_all, k, v, x, y
 
     # the same documents under per-document zigzag: every rank holds two pieces of every
@@ -612,18 +632,16 @@ def extras(np, torch, ra, synth, dev, reps, reps_long):
     oa = torch.randn((rows, h, dd), device=dev, generator=gen)
     ob, la, lb = torch.randn_like(oa), torch.randn((h, rows), device=dev), torch.randn((h, rows), device=dev)
     oo, lo = torch.empty_like(oa), torch.empty_like(la)
-    tm = time_events(torch, lambda: ra.ra_lse_merge(oa, la, ob, lb, o_out=oo, lse_out=lo), reps)
     nbytes = 3 * oa.numel() * 4 + 3 * la.numel() * 4
-    res["lse_merge_8192x32x128_f32"] = {"avg_ms": tm["avg_ms"], "bytes": nbytes, "gbs": gbs(nbytes, tm["avg_ms"]),
-                                        "frac_hbm_peak": gbs(nbytes, tm["avg_ms"]) / PEAK_HBM_GBS}
+    res["lse_merge_8192x32x128_f32"] = time_hbm(torch, lambda: ra.ra_lse_merge(oa, la, ob, lb, o_out=oo, lse_out=lo),
+                                                reps, nbytes)
     del oa, ob, la, lb, oo, lo
 
     # measured ceilings: torch's device-to-device copy of 1 GiB, and the register-only MFMA loop
     src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
-    tc = time_events(torch, lambda: dst.copy_(src), reps)
     nbytes = 2 * src.numel() * 2
-    res["ceiling_torch_copy_1GiB"] = {"avg_ms": tc["avg_ms"], "bytes": nbytes, "gbs": gbs(nbytes, tc["avg_ms"])}
+    res["ceiling_torch_copy_1GiB"] = time_hbm(torch, lambda: dst.copy_(src), reps, nbytes)
     del src, dst
     res["ceiling_mfma_bf16_loop"] = mfma_ceiling(torch, ra)
     log(f"ceilings: copy {res['ceiling_torch_copy_1GiB']['gbs']:.0f} GB/s, "

@@ -350,30 +350,43 @@ __device__ __forceinline__ void merge_weights(float la, float lb, float& wa, flo
   wb = expf(lb - lse);
 }
 
-__global__ void __launch_bounds__(256) lse_merge_vec_kernel(long long rows, int h, int d, const float* o_a,
-                                                            const float* lse_a, const float* o_b, const float* lse_b,
-                                                            float* o_out, float* lse_out) {
+// Four 16-byte chunks per thread: a block covers 4 consecutive spans of 256
+// chunks, and every load is issued (nontemporal) before the first store, so
+// that 8 loads per thread are in flight. A (row, head) pair's d/4 lanes sit in
+// one wave for each span, so in-place merges stay safe.
+typedef float mf32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMergeChunks = 4;
+__global__ void __launch_bounds__(256) lse_merge_vec4_kernel(long long rows, int h, int d, const float* o_a,
+                                                             const float* lse_a, const float* o_b, const float* lse_b,
+                                                             float* o_out, float* lse_out, long long chunks) {
   const int per = d >> 2;  // lanes per (row, head): a power of two <= 64
-  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long pair = gid / per;
-  const int sub = (int)(gid - pair * per);
-  if (pair >= rows * h) return;
-  const long long row = pair / h;
-  const int hh = (int)(pair - row * h);
-  const size_t li = (size_t)hh * rows + row;
-  float wa, wb, lse;
-  merge_weights(lse_a[li], lse_b[li], wa, wb, lse);
-  const size_t oi = (size_t)pair * d + 4 * sub;
-  const float4 a = *(const float4*)(o_a + oi);
-  const float4 b = *(const float4*)(o_b + oi);
-  float4 r;
-  r.x = wa * a.x + wb * b.x;
-  r.y = wa * a.y + wb * b.y;
-  r.z = wa * a.z + wb * b.z;
-  r.w = wa * a.w + wb * b.w;
-  *(float4*)(o_out + oi) = r;
-  if (sub == 0) lse_out[li] = lse;
+  const long long c0 = (long long)blockIdx.x * (256 * kMergeChunks) + threadIdx.x;
+  mf32x4 a[kMergeChunks], b[kMergeChunks];
+  float la[kMergeChunks], lb[kMergeChunks];
+  size_t li[kMergeChunks];
+#pragma unroll
+  for (int k = 0; k < kMergeChunks; ++k) {
+    const long long c = c0 + 256 * k;
+    const long long cc = c < chunks ? c : chunks - 1;  // past the end: a valid chunk, never stored
+    const long long pair = cc / per;
+    const long long row = pair / h;
+    li[k] = (size_t)(pair - row * h) * rows + row;
+    la[k] = lse_a[li[k]];
+    lb[k] = lse_b[li[k]];
+    a[k] = __builtin_nontemporal_load((const mf32x4*)o_a + cc);
+    b[k] = __builtin_nontemporal_load((const mf32x4*)o_b + cc);
+  }
+#pragma unroll
+  for (int k = 0; k < kMergeChunks; ++k) {
+    const long long c = c0 + 256 * k;
+    if (c >= chunks) continue;
+    float wa, wb, lse;
+    merge_weights(la[k], lb[k], wa, wb, lse);
+    __builtin_nontemporal_store(wa * a[k] + wb * b[k], (mf32x4*)o_out + c);
+    if ((c & (per - 1)) == 0) lse_out[li[k]] = lse;
+  }
 }
+
 
 __global__ void __launch_bounds__(256) lse_merge_scalar_kernel(long long rows, int h, int d, const float* o_a,
                                                                const float* lse_a, const float* o_b,
@@ -400,9 +413,10 @@ hipError_t launch_lse_merge(int64_t rows, int h, int d, const float* o_a, const 
   const bool vec = d % 4 == 0 && per <= 64 && (per & (per - 1)) == 0 &&
                    ((uintptr_t)o_a | (uintptr_t)o_b | (uintptr_t)o_out) % 16 == 0;
   if (vec) {
-    const long long threads = pairs * per;
-    hipLaunchKernelGGL(lse_merge_vec_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rows, h, d,
-                       o_a, lse_a, o_b, lse_b, o_out, lse_out);
+    const long long chunks = pairs * per;
+    const long long blocks = (chunks + 256 * kMergeChunks - 1) / (256 * kMergeChunks);
+    hipLaunchKernelGGL(lse_merge_vec4_kernel, dim3((unsigned)blocks), dim3(256), 0, st, rows, h, d, o_a, lse_a, o_b,
+                       lse_b, o_out, lse_out, chunks);
   } else {
     hipLaunchKernelGGL(lse_merge_scalar_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, st, rows, h, d,
                        o_a, lse_a, o_b, lse_b, o_out, lse_out);
@@ -545,6 +559,37 @@ __global__ void __launch_bounds__(256) copy_rows_pow2_kernel(const CopyArgs c, i
   }
 }
 
+// Ulysses forward for runs of at most 8 KiB: one block per (group of G consecutive
+// tokens, head block rho), rho varying fastest across blocks. A block reads the G
+// runs (token, rho) of the source -- n runs apart -- and writes them as one
+// contiguous 8 KiB piece of head block rho, so the blocks in flight write n
+// sequential streams and read one. Two 16-byte chunks per thread.
+constexpr int kUlyChunks = 512;
+__global__ void __launch_bounds__(256) ulysses_fwd_kernel(const CopyArgs c, int log2_cpr) {
+  constexpr int U = kUlyChunks / 256;
+  const u32x4* src = (const u32x4*)c.in;
+  u32x4* dst = (u32x4*)c.out;
+  const int n = c.cp;
+  const long long ntok = (long long)n * c.s_local;
+  const int G = kUlyChunks >> log2_cpr;
+  const long long cmask = (1ll << log2_cpr) - 1;
+  const long long rho = blockIdx.x % n;
+  const long long tok0 = (long long)(blockIdx.x / n) * G;
+  u32x4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = threadIdx.x + 256 * u;
+    const long long tok = tok0 + (q >> log2_cpr);
+    if (tok < ntok) v[u] = __builtin_nontemporal_load(src + (((tok * n + rho) << log2_cpr) | (q & cmask)));
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = threadIdx.x + 256 * u;
+    const long long tok = tok0 + (q >> log2_cpr);
+    if (tok < ntok) __builtin_nontemporal_store(v[u], dst + (((rho * c.bstride + tok) << log2_cpr) | (q & cmask)));
+  }
+}
+
 template <int KIND, bool SCATTER = false>
 static hipError_t launch_copy(const void* in, void* out, long long nrows, long long row_bytes, int s_local, int cp,
                               int part, hipStream_t st, long long bstride = 0) {
@@ -595,11 +640,23 @@ hipError_t launch_ulysses(const void* in, void* out, int n, int64_t s_local, int
                           int64_t block_runs, hipStream_t st) {
   const long long runs = (long long)n * n * s_local;
   if (inverse) return launch_copy<MAP_ULY_INV>(in, out, runs, run_bytes, (int)s_local, n, 0, st, block_runs);
-  // forward: walking the source in order (sequential reads, n write streams) and
-  // scattering with the inverse map beats gathering 2 KB runs at an n-run stride
+  // forward: 16-byte-aligned power-of-two runs of at most 8 KiB take the blocked walk
+  // (contiguous 8 KiB writes per block, head block fastest across blocks); runs of up
+  // to 16 KiB walk the source in order and scatter; anything else gathers row by row
   const uintptr_t al = (uintptr_t)in | (uintptr_t)out | (uintptr_t)run_bytes;
   const long long cpr16 = run_bytes / 16;
-  if (al % 16 == 0 && cpr16 <= 1024 && (cpr16 & (cpr16 - 1)) == 0)
+  const bool pow2 = al % 16 == 0 && cpr16 >= 1 && (cpr16 & (cpr16 - 1)) == 0;
+  if (pow2 && cpr16 <= kUlyChunks && runs > 0) {
+    int lg = 0;
+    while ((1ll << lg) < cpr16) ++lg;
+    const long long G = kUlyChunks / cpr16, ntok = (long long)n * s_local;
+    const long long blocks = ((ntok + G - 1) / G) * n;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    CopyArgs c{in, out, runs, cpr16, (int)s_local, n, 0, block_runs};
+    hipLaunchKernelGGL(ulysses_fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, lg);
+    return hipGetLastError();
+  }
+  if (pow2 && cpr16 <= 1024)
     return launch_copy<MAP_ULY_INV, true>(in, out, runs, run_bytes, (int)s_local, n, 0, st, block_runs);
   return launch_copy<MAP_ULY_FWD>(in, out, runs, run_bytes, (int)s_local, n, 0, st, block_runs);
 }

@@ -148,7 +148,7 @@ def test_steps_partials_and_merge_chain():
 
 def test_lse_merge_kernel_against_oracle():
     rng = np.random.default_rng(3)
-    for rows, h, d in ((37, 3, 128), (5, 2, 6), (64, 4, 64)):
+    for rows, h, d in ((37, 3, 128), (5, 2, 6), (64, 4, 64), (1003, 8, 128)):
         oa, ob = rng.standard_normal((rows, h, d)), rng.standard_normal((rows, h, d))
         la, lb = rng.standard_normal((h, rows)) * 5, rng.standard_normal((h, rows)) * 5
         la[0, :3] = -np.inf
@@ -161,6 +161,10 @@ def test_lse_merge_kernel_against_oracle():
         assert max_abs(o.cpu().numpy(), O) <= 1e-5
         assert max_abs(l.cpu().numpy(), L) <= 1e-5
         assert np.array_equal(np.isneginf(l.cpu().numpy()), np.isneginf(L))
+        # in place (outputs over the first operand) gives the same bits
+        oi, li_ = t(oa), t(la)
+        ra.ra_lse_merge(oi, li_, t(ob), t(lb), o_out=oi, lse_out=li_)
+        assert torch.equal(oi, o) and torch.equal(li_, l)
 
 
 def test_causality_perturbation_is_bit_identical():

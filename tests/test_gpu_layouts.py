@@ -39,7 +39,8 @@ def test_cp_reorder_full_size_bitexact(w):
     assert torch.equal(ra.cp_reorder(y, w.cp, w.partition, inverse=True), qt)
 
 
-@pytest.mark.parametrize("n,sl,h,d", [(1, 5, 3, 2), (2, 7, 4, 3), (4, 9, 8, 64), (8, 3, 8, 5)])
+@pytest.mark.parametrize("n,sl,h,d", [(1, 5, 3, 2), (2, 7, 4, 3), (4, 9, 8, 64), (8, 3, 8, 5), (2, 5, 64, 128),
+                                     (2, 3, 128, 128), (4, 37, 4, 128)])
 def test_ulysses_small_bitexact(n, sl, h, d):
     x = np.random.default_rng(n).integers(0, 1 << 16, (n, sl, h, d)).astype(np.uint16)
     xt = to_device(x, "bf16")
