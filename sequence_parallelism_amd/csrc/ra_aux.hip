@@ -559,18 +559,21 @@ __global__ void __launch_bounds__(256) copy_rows_pow2_kernel(const CopyArgs c, i
   }
 }
 
-// Ulysses forward for runs of at most 8 KiB: one block per (group of G consecutive
-// tokens, head block rho), rho varying fastest across blocks. A block reads the G
-// runs (token, rho) of the source -- n runs apart -- and writes them as one
-// contiguous 8 KiB piece of head block rho, so the blocks in flight write n
-// sequential streams and read one. Two 16-byte chunks per thread.
+// Strided transpose of runs, dst run (rho * bstride + tok) <- src run (tok * n + rho)
+// for tok < nrows / n and rho < n: the Ulysses forward (runs of hq / n heads, tokens
+// of all n source ranks) and the striped CP reorder (runs are rows, rho the rank).
+// For runs of at most 8 KiB: one block per (group of G consecutive tokens, rho),
+// rho varying fastest across blocks. A block reads the G runs (tok, rho) of the
+// source -- n runs apart -- and writes them as one contiguous 8 KiB piece, so the
+// blocks in flight write n sequential streams and read one. Two 16-byte chunks
+// per thread.
 constexpr int kUlyChunks = 512;
 __global__ void __launch_bounds__(256) ulysses_fwd_kernel(const CopyArgs c, int log2_cpr) {
   constexpr int U = kUlyChunks / 256;
   const u32x4* src = (const u32x4*)c.in;
   u32x4* dst = (u32x4*)c.out;
   const int n = c.cp;
-  const long long ntok = (long long)n * c.s_local;
+  const long long ntok = c.nrows / n;
   const int G = kUlyChunks >> log2_cpr;
   const long long cmask = (1ll << log2_cpr) - 1;
   const long long rho = blockIdx.x % n;
@@ -629,10 +632,34 @@ static hipError_t launch_copy(const void* in, void* out, long long nrows, long l
   return hipGetLastError();
 }
 
+// The strided transpose above for 16-byte-aligned power-of-two runs of at most 8 KiB
+// (nruns = n * tokens); false when the runs do not fit it.
+static bool launch_strided_transpose(const void* in, void* out, long long nruns, long long run_bytes, int n,
+                                     long long bstride, hipStream_t st, hipError_t& err) {
+  const uintptr_t al = (uintptr_t)in | (uintptr_t)out | (uintptr_t)run_bytes;
+  const long long cpr16 = run_bytes / 16;
+  if (al % 16 != 0 || cpr16 < 1 || cpr16 > kUlyChunks || (cpr16 & (cpr16 - 1)) != 0 || nruns <= 0) return false;
+  int lg = 0;
+  while ((1ll << lg) < cpr16) ++lg;
+  const long long G = kUlyChunks / cpr16, ntok = nruns / n;
+  const long long blocks = ((ntok + G - 1) / G) * n;
+  if (blocks > 0x7fffffffLL) {
+    err = hipErrorInvalidValue;
+    return true;
+  }
+  CopyArgs c{in, out, nruns, cpr16, 0, n, 0, bstride};
+  hipLaunchKernelGGL(ulysses_fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, lg);
+  err = hipGetLastError();
+  return true;
+}
+
 hipError_t launch_cp_reorder(const void* in, void* out, int64_t s, int64_t row_bytes, int cp, int part, int inverse,
                              hipStream_t st) {
   const int s_local = (int)(s / cp);
   if (inverse) return launch_copy<MAP_REORDER_INV>(in, out, s, row_bytes, s_local, cp, part, st);
+  // striped: rank r's row i is global row i cp + r, the strided transpose with n = cp
+  hipError_t e;
+  if (part == PART_STRIPED && launch_strided_transpose(in, out, s, row_bytes, cp, s_local, st, e)) return e;
   return launch_copy<MAP_REORDER_FWD>(in, out, s, row_bytes, s_local, cp, part, st);
 }
 
@@ -643,19 +670,11 @@ hipError_t launch_ulysses(const void* in, void* out, int n, int64_t s_local, int
   // forward: 16-byte-aligned power-of-two runs of at most 8 KiB take the blocked walk
   // (contiguous 8 KiB writes per block, head block fastest across blocks); runs of up
   // to 16 KiB walk the source in order and scatter; anything else gathers row by row
+  hipError_t e;
+  if (launch_strided_transpose(in, out, runs, run_bytes, n, block_runs, st, e)) return e;
   const uintptr_t al = (uintptr_t)in | (uintptr_t)out | (uintptr_t)run_bytes;
   const long long cpr16 = run_bytes / 16;
   const bool pow2 = al % 16 == 0 && cpr16 >= 1 && (cpr16 & (cpr16 - 1)) == 0;
-  if (pow2 && cpr16 <= kUlyChunks && runs > 0) {
-    int lg = 0;
-    while ((1ll << lg) < cpr16) ++lg;
-    const long long G = kUlyChunks / cpr16, ntok = (long long)n * s_local;
-    const long long blocks = ((ntok + G - 1) / G) * n;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    CopyArgs c{in, out, runs, cpr16, (int)s_local, n, 0, block_runs};
-    hipLaunchKernelGGL(ulysses_fwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, c, lg);
-    return hipGetLastError();
-  }
   if (pow2 && cpr16 <= 1024)
     return launch_copy<MAP_ULY_INV, true>(in, out, runs, run_bytes, (int)s_local, n, 0, st, block_runs);
   return launch_copy<MAP_ULY_FWD>(in, out, runs, run_bytes, (int)s_local, n, 0, st, block_runs);
