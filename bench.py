@@ -119,13 +119,37 @@ def mall_flush(torch):
     _FLUSH[0].sum()
 
 
-def time_hbm(torch, fn, reps, nbytes):
-    """An HBM-bound kernel timed with the cache flushed before every repetition:
-    average, minimum and median, and GB/s at the average and at the minimum."""
-    t = time_events(torch, fn, reps, flush=lambda: mall_flush(torch))
-    return {"avg_ms": t["avg_ms"], "min_ms": t["min_ms"], "median_ms": t["median_ms"], "bytes": nbytes,
-            "gbs": gbs(nbytes, t["avg_ms"]), "gbs_best": gbs(nbytes, t["min_ms"]),
-            "frac_hbm_peak": gbs(nbytes, t["avg_ms"]) / PEAK_HBM_GBS}
+ROTATE_BYTES = 2 << 30
+
+
+def rotating_sets(nbytes):
+    """Buffer sets for time_hbm: enough that the launches between two uses of one
+    set move at least 2 GiB, eight times the 256 MB last-level cache."""
+    return max(1, min(8, -(-ROTATE_BYTES // nbytes)))
+
+
+def time_hbm(torch, fns, reps, nbytes):
+    """An HBM-bound kernel timed cold. `fns` holds one call per buffer set (see
+    rotating_sets). Each repetition flushes the cache, then runs every set once,
+    back to back, between two events: no launch finds its data in the cache, and
+    the events' own latency is shared by the launches of the stream, as in a run of
+    reorders of Q, K and V. avg/min/median are per launch. The `single_launch`
+    figures time the first set alone after each flush, event latency included."""
+    if callable(fns):
+        fns = [fns]
+
+    def stream():
+        for f in fns:
+            f()
+
+    t = time_events(torch, stream, reps, flush=lambda: mall_flush(torch))
+    n = len(fns)
+    one = time_events(torch, fns[0], reps, flush=lambda: mall_flush(torch))
+    return {"avg_ms": t["avg_ms"] / n, "min_ms": t["min_ms"] / n, "median_ms": t["median_ms"] / n, "bytes": nbytes,
+            "gbs": gbs(nbytes, t["avg_ms"] / n), "gbs_best": gbs(nbytes, t["min_ms"] / n),
+            "frac_hbm_peak": gbs(nbytes, t["avg_ms"] / n) / PEAK_HBM_GBS, "buffer_sets": n,
+            "single_launch": {"avg_ms": one["avg_ms"], "gbs": gbs(nbytes, one["avg_ms"]),
+                              "frac_hbm_peak": gbs(nbytes, one["avg_ms"]) / PEAK_HBM_GBS}}
 
 
 def traffic_from_profiles(kernel_src_sha):
@@ -147,6 +171,13 @@ def kernel_source_sha():
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "sequence_parallelism_amd", "csrc", f), "rb").read())
     return h.hexdigest()
+
+
+def reorder_call(torch, ra, like, cp, partition):
+    """cp_reorder of a fresh copy of `like` into a fresh output: one more buffer set for time_hbm."""
+    x = like.clone()
+    y = torch.empty((cp, like.shape[0] // cp) + tuple(like.shape[1:]), dtype=like.dtype, device=like.device)
+    return lambda: ra.cp_reorder(x, cp, partition, out=y)
 
 
 def gbs(nbytes, ms):
@@ -512,8 +543,9 @@ def extras(np, torch, ra, synth, dev, reps, reps_long):
                                              "tflops": fl / (ta["avg_ms"] * 1e-3) / 1e12,
                                              "frac_bf16_peak": fl / (ta["avg_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     nbytes = 2 * k_g.numel() * 2
-    res["cp_reorder_s32k_h32_zigzag"] = time_hbm(torch, lambda: ra.cp_reorder(k_g, cp, w.partition, out=k_p), reps,
-                                                 nbytes)
+    res["cp_reorder_s32k_h32_zigzag"] = time_hbm(
+        torch, [lambda: ra.cp_reorder(k_g, cp, w.partition, out=k_p)] +
+        [reorder_call(torch, ra, k_g, cp, w.partition) for _ in range(rotating_sets(nbytes) - 1)], reps, nbytes)
 
     # backward of the same share: dQ, and this rank's dK / dV partials of every chunk
     log("extras: backward of the zigzag share")
@@ -544,7 +576,8 @@ def extras(np, torch, ra, synth, dev, reps, reps_long):
         y = torch.empty((w.cp, slg, h, w.d), dtype=torch.bfloat16, device=dev)
         nbytes = 2 * x.numel() * 2
         res[f"cp_reorder_s64k_h{h}_striped_{tag}"] = time_hbm(
-            torch, lambda: ra.cp_reorder(x, w.cp, w.partition, out=y), reps, nbytes)
+            torch, [lambda: ra.cp_reorder(x, w.cp, w.partition, out=y)] +
+            [reorder_call(torch, ra, x, w.cp, w.partition) for _ in range(rotating_sets(nbytes) - 1)], reps, nbytes)
         del x, y
     del q, k, v
 
@@ -633,8 +666,15 @@ def extras(np, torch, ra, synth, dev, reps, reps_long):
     ob, la, lb = torch.randn_like(oa), torch.randn((h, rows), device=dev), torch.randn((h, rows), device=dev)
     oo, lo = torch.empty_like(oa), torch.empty_like(la)
     nbytes = 3 * oa.numel() * 4 + 3 * la.numel() * 4
-    res["lse_merge_8192x32x128_f32"] = time_hbm(torch, lambda: ra.ra_lse_merge(oa, la, ob, lb, o_out=oo, lse_out=lo),
-                                                reps, nbytes)
+
+    def merge_call():
+        a, b, o = torch.randn_like(oa), torch.randn_like(oa), torch.empty_like(oa)
+        sa, sb, so = torch.randn_like(la), torch.randn_like(la), torch.empty_like(la)
+        return lambda: ra.ra_lse_merge(a, sa, b, sb, o_out=o, lse_out=so)
+
+    res["lse_merge_8192x32x128_f32"] = time_hbm(
+        torch, [lambda: ra.ra_lse_merge(oa, la, ob, lb, o_out=oo, lse_out=lo)] +
+        [merge_call() for _ in range(rotating_sets(nbytes) - 1)], reps, nbytes)
     del oa, ob, la, lb, oo, lo
 
     # measured ceilings: torch's device-to-device copy of 1 GiB, and the register-only MFMA loop
