@@ -357,10 +357,10 @@ class Plan:
     s_local is the rank's local length; cu (a host int32 array, or None) the
     documents a per-document zigzag plan was made for."""
 
-    def __init__(self, shape, n_docs, cp_size, rank, partition, workspace, ws_bytes, s_local, cu=None):
+    def __init__(self, shape, n_docs, cp_size, rank, partition, workspace, ws_bytes, s_local, cu=None, stream=None):
         self.shape, self.n_docs, self.cp_size, self.rank = shape, n_docs, cp_size, rank
         self.partition, self.workspace, self.ws_bytes = partition, workspace, ws_bytes
-        self.s_local, self.cu = s_local, cu
+        self.s_local, self.cu, self.stream = s_local, cu, stream
 
 
 def ra_plan(s_total: int, hq: int, hkv: int, d: int, cu_seqlens=None, cp_size: int = 1, rank: int = 0,
@@ -378,7 +378,8 @@ def ra_plan(s_total: int, hq: int, hkv: int, d: int, cu_seqlens=None, cp_size: i
     dev = torch.device(device) if workspace is None else _same_gpu(("workspace", workspace))
     if dev.type != "cuda":
         raise ValueError(f"device {dev}: the plan lives on a GPU")
-    with _On(stream) as st:
+    on = _On(stream)
+    with on as st:
         ws, ws_bytes = _workspace(need, dev, workspace)
         status = load_library().ra_plan(ctypes.byref(shape), cu_ptr, n_docs, int(cp_size), int(rank),
                                         _part(partition), _ptr(ws), ws_bytes, st)
@@ -386,7 +387,7 @@ def ra_plan(s_total: int, hq: int, hkv: int, d: int, cu_seqlens=None, cp_size: i
     part = _part(partition)
     s_l = ra_local_length(s_total, cp_size, partition, cu_seqlens)
     return Plan(shape, n_docs, int(cp_size), int(rank), part, ws, ws_bytes, s_l,
-                cu_arr if part == RA_PART_DOC_ZIGZAG else None)
+                cu_arr if part == RA_PART_DOC_ZIGZAG else None, on.s)
 
 
 def ra_forward_planned(q, k, v, plan: Plan, *, out=None, lse=None, stream=None):
@@ -405,7 +406,12 @@ def ra_forward_planned(q, k, v, plan: Plan, *, out=None, lse=None, stream=None):
     if lse is not None:
         _need(lse, "lse", (sh.hq, s_l), torch.float32)
     dev = _same_gpu(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("plan workspace", plan.workspace))
-    with _On(stream) as st:
+    on = _On(stream)
+    if plan.stream is not None and on.s != plan.stream:
+        # the workspace may come from the allocator on the plan's stream: keep it
+        # from being handed out again before this launch has read it
+        plan.workspace.record_stream(on.s)
+    with on as st:
         if out is None:
             out = torch.empty((s_l, sh.hq, sh.d), dtype=out_dtype, device=dev)
         if lse is None:

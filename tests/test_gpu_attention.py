@@ -226,3 +226,27 @@ def test_side_stream_launch_matches_the_current_stream():
                          stream=side.cuda_stream)
     torch.cuda.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_plan_used_on_another_stream_after_it_is_dropped():
+    """A plan built on the current stream, then executed on a side stream (after the
+    side stream waits for the plan), then dropped while that launch may still read
+    it: the plan's workspace is recorded on the side stream, so the allocator does
+    not hand it to the current stream's next allocations before the launch ends."""
+    g = _case_inputs(8192, 8, 2, 128, "bf16", seed=29)
+    cp, rank, part = 4, 1, "zigzag"
+    qr, kr, vr = rank_inputs(g, cp, rank, part)
+    ref_o, ref_l = ra.ra_forward(qr, kr, vr, None, cp, rank, part, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        plan = ra.ra_plan(8192, 8, 2, 128, None, cp, rank, part, out_dtype=torch.float32)
+        side.wait_stream(torch.cuda.current_stream())
+        outs.append(ra.ra_forward_planned(qr, kr, vr, plan, stream=side))
+        del plan
+        junk = [torch.full((1 << 20,), -1, dtype=torch.int32, device="cuda") for _ in range(8)]
+        del junk
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
