@@ -274,3 +274,20 @@ def test_step_partial_empty_rows():
     for s, O_t, L_t in parts[1:]:
         assert np.all(O_t == 0) and np.all(np.isneginf(L_t))
     assert [p[0] for p in parts] == [0, 3, 2, 1]
+
+
+def test_ring_chunk_order_follows_the_send_to_next_ring():
+    """[CP-TE] 2.2 and [SP-concept] (Ring Attention): at every step each rank sends
+    the KV chunk it holds to the next rank and receives the previous rank's. The
+    hand-simulated passing gives the chunk each rank holds at each step; the tiny
+    ring simulation's rank 2 of 4 visits chunks 2, 1, 0, 3."""
+    for cp in (1, 2, 3, 4, 8):
+        held = list(range(cp))
+        seen = [[] for _ in range(cp)]
+        for _ in range(cp):
+            for r in range(cp):
+                seen[r].append(held[r])
+            held = [held[(r - 1) % cp] for r in range(cp)]  # receive from the previous rank
+        for r in range(cp):
+            assert oracle.ring_chunk_order(cp, r) == seen[r]
+    assert oracle.ring_chunk_order(4, 2) == [2, 1, 0, 3]
