@@ -2,8 +2,10 @@
 (a dropped term, a wrong base, a mis-mapped head, a mask or partition off by one,
 unnormalised merge weights, a reversed ring) and in the backward (a dropped D
 term, a flipped sign, a wrong operand or scale, a gradient off by 1e-4, GQA
-groups not summed) is put into the oracle by monkeypatching, and at least one of
-its pins must then fail. Without a planted mistake every pin passes.
+groups not summed) and in the layouts (Ulysses head or token order, a reorder
+inverse off by a rank, ragged tiles, the per-document zigzag's bounds and pair
+rotation) is put into the oracle by monkeypatching, and at least one of its pins
+must then fail. Without a planted mistake every pin passes.
 
 The mistakes are planted in the oracle only, on the CPU. The pins compare it with
 independent references (the pure-Python brute force, torch's fp64 SDPA, closed
@@ -207,3 +209,126 @@ def test_the_restated_chain_rule_without_a_slip_passes(monkeypatch):
 def test_planted_backward_slip_fails_a_pin(slip, monkeypatch):
     monkeypatch.setattr(bwd_mod, "attention_rows_backward", _rows_backward_with(slip))
     assert _failing_bwd_pins(), f"no pin notices: {slip}"
+
+
+# ---------------------------------------------------------------------------
+# Layouts, classification and the per-document zigzag map.
+# ---------------------------------------------------------------------------
+import oracle.classify as cls_mod  # noqa: E402
+import oracle.layouts as lay_mod  # noqa: E402
+from tests import test_oracle_doc_zigzag as doc_pins  # noqa: E402
+from tests import test_oracle_layouts as lay_pins  # noqa: E402
+
+_orig_ulysses = lay_mod.ulysses_permute
+_orig_reorder = lay_mod.cp_reorder
+_orig_classify = cls_mod.classify_tiles
+_orig_bounds = part_mod.doc_zigzag_piece_bounds
+_orig_runs = part_mod.doc_zigzag_rank_runs
+
+
+def _ulysses_heads_interleaved(x, n, inverse=False):
+    # device rho takes heads rho, rho + n, ... instead of the block [rho H/n, (rho+1) H/n)
+    x = np.asarray(x)
+    if inverse:
+        return _orig_ulysses(x, n, inverse)
+    N, sl, H, d = x.shape
+    perm = [h2 * n + rho for rho in range(n) for h2 in range(H // n)]
+    return _orig_ulysses(x[:, :, perm], n)
+
+
+def _ulysses_tokens_by_local_index(x, n, inverse=False):
+    # tokens ordered by local index, then source rank
+    y = _orig_ulysses(x, n, inverse)
+    if inverse:
+        return y
+    N, S = y.shape[:2]
+    sl = S // n
+    order = [j * sl + i for i in range(sl) for j in range(n)]
+    return y[:, order]
+
+
+def _reorder_inverse_shifted(x, cp, partition, inverse=False, cu_seqlens=None, s_total=None):
+    # the inverse takes rank r's rows from rank r - 1's slot
+    if not inverse:
+        return _orig_reorder(x, cp, partition, inverse, cu_seqlens, s_total)
+    return _orig_reorder(np.roll(np.asarray(x), 1, axis=0), cp, partition, True, cu_seqlens, s_total)
+
+
+def _classify_edges_as_full_tiles(s_total, cp, rank, partition, cu_seqlens, bm, bn, causal=True,
+                                  return_counts=False):
+    # edge tiles compared with a whole bm x bn tile: a fully visible ragged tile reads PARTIAL
+    cls, counts = _orig_classify(s_total, cp, rank, partition, cu_seqlens, bm, bn, causal, True)
+    cls = np.where(counts == 0, 0, np.where(counts == bm * bn, 2, 1)).astype(np.int8)
+    return (cls, counts) if return_counts else cls
+
+
+def _bounds_rounded_down(L, cp, g=part_mod.DOC_GRANULE):
+    n = 2 * cp
+    k = np.arange(n + 1, dtype=np.int64)
+    b = np.minimum(g * ((k * L) // (n * g)), L)
+    b[n] = L
+    return b
+
+
+def _runs_pairs_not_rotated(cu_seqlens, s_total, cp, rank, g=part_mod.DOC_GRANULE):
+    # every document gives rank r the same pair (r, 2CP-1-r): no rotation by document
+    cu = np.asarray([0, s_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    runs = []
+    for j in range(len(cu) - 1):
+        b = part_mod.doc_zigzag_piece_bounds(int(cu[j + 1] - cu[j]), cp, g)
+        for piece in (rank, 2 * cp - 1 - rank):
+            n_tok = int(b[piece + 1] - b[piece])
+            if n_tok > 0:
+                runs.append((int(cu[j] + b[piece]), n_tok, g * -(-n_tok // g)))
+    return runs
+
+
+LAYOUT_MISTAKES = {
+    "Ulysses heads interleaved": [(lay_mod, "ulysses_permute", _ulysses_heads_interleaved),
+                                  (oracle, "ulysses_permute", _ulysses_heads_interleaved)],
+    "Ulysses tokens by local index": [(lay_mod, "ulysses_permute", _ulysses_tokens_by_local_index),
+                                      (oracle, "ulysses_permute", _ulysses_tokens_by_local_index)],
+    "cp_reorder inverse reads the wrong rank": [(lay_mod, "cp_reorder", _reorder_inverse_shifted),
+                                                (oracle, "cp_reorder", _reorder_inverse_shifted)],
+    "edge tiles classified as whole tiles": [(cls_mod, "classify_tiles", _classify_edges_as_full_tiles),
+                                             (oracle, "classify_tiles", _classify_edges_as_full_tiles)],
+    "doc-zigzag bounds rounded down": [(part_mod, "doc_zigzag_piece_bounds", _bounds_rounded_down),
+                                       (doc_pins, "doc_zigzag_piece_bounds", _bounds_rounded_down)],
+    "doc-zigzag pairs not rotated by document": [(part_mod, "doc_zigzag_rank_runs", _runs_pairs_not_rotated),
+                                                 (doc_pins, "doc_zigzag_rank_runs", _runs_pairs_not_rotated)],
+}
+
+LAYOUT_PINS = {
+    "Ulysses worked layout (golden)": lay_pins.test_ulysses_worked_layout_golden,
+    "Ulysses element indexing": lambda: lay_pins.test_ulysses_inverse_roundtrip_and_indexing(4, 6, 8, 3),
+    "cp_reorder against brute positions": lambda: lay_pins.test_cp_reorder_against_brute_positions("zigzag", 4),
+    "classification against brute force": lambda: lay_pins.test_classify_matches_brute_force(
+        "striped", 2, True, (3, 5), True),
+    "classification of ragged tiles": lambda: lay_pins.test_classify_matches_brute_force(
+        "contiguous", 2, False, (3, 5), False),
+    "doc-zigzag positions against brute force": lambda: doc_pins.test_positions_match_brute_force_and_cover_once(
+        5, 2),
+    "doc-zigzag piece bounds": lambda: doc_pins.test_piece_bounds(5000, 3),
+    "doc-zigzag balance": doc_pins.test_doc_zigzag_balances_packed_documents,
+}
+
+
+def _failing_layout_pins():
+    failed = []
+    for name, pin in LAYOUT_PINS.items():
+        try:
+            pin()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+def test_every_layout_pin_passes_on_the_oracle_as_written():
+    assert _failing_layout_pins() == []
+
+
+@pytest.mark.parametrize("mistake", list(LAYOUT_MISTAKES))
+def test_planted_layout_mistake_fails_a_pin(mistake, monkeypatch):
+    for module, name, fn in LAYOUT_MISTAKES[mistake]:
+        monkeypatch.setattr(module, name, fn)
+    assert _failing_layout_pins(), f"no pin notices: {mistake}"
