@@ -281,7 +281,9 @@ ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_doc
 ra_status check_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, const float* lse_a, const float* o_b,
                           const float* lse_b, const float* o_out, const float* lse_out) {
   if (rows < 0 || h < 1 || d < 1) return RA_ERR_SHAPE;
-  if (rows > ((int64_t)1 << 40) / ((int64_t)h * d)) return RA_ERR_SHAPE;
+  // at most 2^37 elements per tensor (512 GiB of fp32, beyond any one GPU): the
+  // launch grids (one thread per (row, head) pair, or per 4 x 16 bytes) stay in range
+  if (rows > ((int64_t)1 << 37) / ((int64_t)h * d)) return RA_ERR_SHAPE;
   if (rows == 0) return RA_OK;
   if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return RA_ERR_NULL;
   return RA_OK;

@@ -129,6 +129,8 @@ def test_forward_steps_and_merge_validation():
     assert lib.ra_lse_merge(10, 0, 128, P, P, P, P, P, P, None) == ra.RA_ERR_SHAPE
     assert lib.ra_lse_merge(10, 4, 128, None, P, P, P, P, P, None) == ra.RA_ERR_NULL
     assert lib.ra_lse_merge(0, 4, 128, None, None, None, None, None, None, None) == ra.RA_OK
+    # the launch grids are bounded: more than 2^37 elements per tensor is refused
+    assert lib.ra_lse_merge((1 << 37) // 128 + 1, 1, 128, P, P, P, P, P, P, None) == ra.RA_ERR_SHAPE
 
 
 def test_classify_validation():
