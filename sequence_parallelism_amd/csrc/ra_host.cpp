@@ -265,6 +265,13 @@ ra_status check_classify(const ra_shape* shape, const int32_t* cu, int32_t n_doc
   s = check_cu(cu, n_docs, shape->s_total);
   if (s != RA_OK) return s;
   const int32_t nd = effective_docs(cu, n_docs);
+  {
+    // one launch thread per (step, query tile, key tile): at most 2^36 classes
+    const int64_t sl = local_len(shape, cp_size, partition, cu, n_docs);
+    if (sl < 1) return RA_ERR_SHAPE;
+    const int64_t nqt = (sl + bm - 1) / bm, nkt = (sl + bn - 1) / bn;
+    if (nqt > ((int64_t)1 << 36) / nkt / cp_size) return RA_ERR_SHAPE;
+  }
   size_t need = nd > 1 ? (size_t)(nd + 1) * 4 : 0;
   if (partition == RA_PART_DOC_ZIGZAG) {
     // tiles must not span more than two 64-slot blocks

@@ -143,6 +143,9 @@ def test_classify_validation():
         == ra.RA_ERR_DIVISIBILITY
     cu = (ctypes.c_int32 * 3)(0, 100, 4096)
     assert lib.ra_classify(ctypes.byref(sh), cu, 2, 4, 0, 1, 64, 64, P, None, 0, None) == ra.RA_ERR_WORKSPACE
+    # more than 2^36 tile classes (one launch thread each) is refused
+    big = shape(s_total=1 << 20)
+    assert lib.ra_classify(ctypes.byref(big), None, 0, 1, 0, 0, 1, 8, P, P, 0, None) == ra.RA_ERR_SHAPE
     bad = (ctypes.c_int32 * 3)(0, 5000, 4096)
     assert lib.ra_classify(ctypes.byref(sh), bad, 2, 4, 0, 1, 64, 64, P, P, 64, None) == ra.RA_ERR_CU_SEQLENS
 
