@@ -639,6 +639,19 @@ def extras(np, torch, ra, synth, dev, reps, reps_long):
         "note": "avg_ms: ra_forward_planned on a prebuilt plan per rank (as the global zigzag ranks); "
                 "avg_ms_with_plan: ra_forward per rank (plan included)"}
     del q_all, k, v, dws, dout, dlse
+    # the per-document zigzag reorder of a global [131072, 32, 128] tensor into the 8
+    # ranks' padded shares (padding slots are written as zeros, so they count as bytes)
+    xg = _randn(torch, gen, dev, w.s_total, w.hq, w.d)
+    row_bytes = w.hq * w.d * 2
+    nbytes = (w.s_total + w.cp * sld) * row_bytes
+
+    def docs_call():
+        x, y = xg.clone(), torch.empty((w.cp, sld, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+        return lambda: ra.cp_reorder_docs(x, w.cp, cu, out=y)
+
+    res["cp_reorder_docs_s128k_h32"] = time_hbm(
+        torch, [docs_call() for _ in range(rotating_sets(nbytes))], reps, nbytes)
+    del xg
 
     # Ulysses x Ring hybrid: a 4 x 2 grid (Ulysses 4 inside, zigzag ring of 2 across), S=131072,
     # 32 heads; the whole grid's work on one GPU (all 8 devices' permutes and attention)

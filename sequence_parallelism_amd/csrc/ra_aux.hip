@@ -272,9 +272,68 @@ __global__ void __launch_bounds__(256) copy_doc_rows_kernel(const DocCopyArgs c)
   }
 }
 
+// 16-byte-aligned rows of a power-of-two number of chunks: the rank-major side is
+// walked as one flat array of 16-byte chunks (the destination of the forward, the
+// source of the inverse), each thread keeping kDocUnroll nontemporal loads in
+// flight, as the other permutations do; a chunk's row maps through its block
+// descriptor, and padding slots read as zeros (forward) or are skipped (inverse).
+constexpr int kDocUnroll = 4;
+
+template <bool INVERSE>
+__global__ void __launch_bounds__(256) copy_doc_pow2_kernel(const DocCopyArgs c, int log2_cpr) {
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  const u4* src = (const u4*)c.in;
+  u4* dst = (u4*)c.out;
+  const long long total = c.nrows << log2_cpr;
+  const long long cmask = (1ll << log2_cpr) - 1;
+  const long long step = (long long)gridDim.x * 256 * kDocUnroll;
+  for (long long base = (long long)blockIdx.x * 256 * kDocUnroll + threadIdx.x; base < total; base += step) {
+    u4 v[kDocUnroll];
+    long long g[kDocUnroll];
+#pragma unroll
+    for (int u = 0; u < kDocUnroll; ++u) {
+      const long long idx = base + u * 256;
+      g[u] = -1;
+      v[u] = u4{0u, 0u, 0u, 0u};
+      if (idx < total) {
+        g[u] = doc_global_row(c, idx >> log2_cpr);
+        if (INVERSE) {
+          v[u] = __builtin_nontemporal_load(src + idx);
+        } else if (g[u] >= 0) {
+          v[u] = __builtin_nontemporal_load(src + ((g[u] << log2_cpr) | (idx & cmask)));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDocUnroll; ++u) {
+      const long long idx = base + u * 256;
+      if (idx < total) {
+        if (!INVERSE) {
+          dst[idx] = v[u];
+        } else if (g[u] >= 0) {
+          dst[(g[u] << log2_cpr) | (idx & cmask)] = v[u];
+        }
+      }
+    }
+  }
+}
+
 template <bool INVERSE>
 static hipError_t launch_doc_copy(DocCopyArgs c, long long row_bytes, hipStream_t st) {
   if (c.nrows == 0 || row_bytes == 0) return hipSuccess;
+  {
+    const uintptr_t al = (uintptr_t)c.in | (uintptr_t)c.out | (uintptr_t)row_bytes;
+    const long long cpr16 = row_bytes / 16;
+    if (al % 16 == 0 && cpr16 <= 1024 && (cpr16 & (cpr16 - 1)) == 0) {
+      int lg = 0;
+      while ((1ll << lg) < cpr16) ++lg;
+      long long blocks = ((c.nrows << lg) + 256 * kDocUnroll - 1) / (256 * kDocUnroll);
+      if (blocks > 65536) blocks = 65536;
+      c.cpr = cpr16;
+      hipLaunchKernelGGL((copy_doc_pow2_kernel<INVERSE>), dim3((unsigned)blocks), dim3(256), 0, st, c, lg);
+      return hipGetLastError();
+    }
+  }
   long long blocks = (c.nrows + 3) / 4;
   if (blocks > 65536) blocks = 65536;
   const uintptr_t al = (uintptr_t)c.in | (uintptr_t)c.out | (uintptr_t)row_bytes;
