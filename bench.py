@@ -244,7 +244,7 @@ def main():
     ap.add_argument("--rank", type=int, default=None, help="attn-only: the rank (default: the headline rank; -1: every rank in turn)")
     ap.add_argument("--which", default="ulysses_fwd",
                     choices=["ulysses_fwd", "ulysses_inv", "reorder_llama7b", "reorder_gqa_q", "reorder_gqa_kv",
-                             "reorder_packed"])
+                             "reorder_packed", "reorder_docs"])
     ap.add_argument("--launches", type=int, default=12, help="launches in the single-kernel modes")
     args = ap.parse_args()
 
@@ -463,6 +463,14 @@ def permute_only(np, torch, ra, synth, dev, which, launches):
         else:
             fn = lambda: ra.ulysses_permute(y, U_N, inverse=True, out=x)  # noqa: E731
         nbytes = 2 * x.numel() * 2
+    elif which == "reorder_docs":
+        w = synth.PACKED_ZIGZAG
+        cu = synth.loguniform_cu_seqlens(0, w.s_total, w.doc_lo, w.doc_hi)
+        x = _randn(torch, gen, dev, w.s_total, w.hq, w.d)
+        sld = ra.ra_local_length(w.s_total, w.cp, "doc_zigzag", cu)
+        y = torch.empty((w.cp, sld, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+        fn = lambda: ra.cp_reorder_docs(x, w.cp, cu, out=y)  # noqa: E731
+        nbytes = (w.s_total + w.cp * sld) * w.hq * w.d * 2
     else:
         w, h = {"reorder_llama7b": (synth.LLAMA7B_ZIGZAG, 32), "reorder_gqa_q": (synth.GQA_STRIPED, 32),
                 "reorder_gqa_kv": (synth.GQA_STRIPED, 8), "reorder_packed": (synth.PACKED_ZIGZAG, 32)}[which]
