@@ -252,7 +252,8 @@ ra_status ra_backward(const void* q, const void* k, const void* v, const void* o
  * -inf marks an empty partial (weight 0); two empty partials give (0, -inf).
  *   o_a, o_b, o_out      device fp32 [rows][h][d]
  *   lse_a, lse_b, lse_out device fp32 [h][rows]
- * o_out may alias o_a or o_b and lse_out may alias lse_a or lse_b (in place). */
+ * o_out may alias o_a or o_b and lse_out may alias lse_a or lse_b (in place).
+ * rows * h * d above 2^37 gives RA_ERR_SHAPE. */
 ra_status ra_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, const float* lse_a,
                        const float* o_b, const float* lse_b, float* o_out, float* lse_out, void* stream);
 
@@ -264,7 +265,8 @@ ra_status ra_lse_merge(int64_t rows, int32_t h, int32_t d, const float* o_a, con
  * shape supplies s_total and causal (heads and dtypes are not used).
  * bm, bn in [1, 65536]; RA_PART_DOC_ZIGZAG: bm, bn in {16, 32, 64, 128}, the
  * grid is over S_l = ra_local_length(), a tile holding padding is never FULL,
- * and the workspace must hold ra_doc_workspace_size() bytes. */
+ * and the workspace must hold ra_doc_workspace_size() bytes. More than 2^36
+ * classes (cp x tiles) gives RA_ERR_SHAPE. */
 ra_status ra_classify(const ra_shape* shape, const int32_t* cu_seqlens, int32_t n_docs, int32_t cp_size,
                       int32_t rank, int32_t partition, int32_t bm, int32_t bn, int8_t* cls, void* workspace,
                       size_t ws_bytes, void* stream);
