@@ -96,7 +96,8 @@ def test_ragged_tiles_and_noncausal(part):
 
 
 @pytest.mark.parametrize("S,cp,part", [(16, 1, "contiguous"), (64, 1, "contiguous"), (100, 1, "contiguous"),
-                                       (128, 2, "zigzag"), (200, 2, "striped"), (384, 3, "zigzag")])
+                                       (128, 2, "zigzag"), (200, 2, "striped"), (384, 3, "zigzag"),
+                                       (256, 16, "contiguous"), (384, 64, "zigzag"), (320, 64, "striped")])
 def test_short_work_lists(S, cp, part):
     """Query tiles whose work lists hold one or two entries (the head_dim-128 kernel
     still loads tiles two entries ahead, past the end of the list) and ragged key

@@ -61,6 +61,15 @@ def test_backward_head_dims_and_output_dtypes(d, out_bf16):
     check_rank(g, gdo, 2, 1, "zigzag", out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
 
 
+@pytest.mark.parametrize("S,cp,part", [(256, 16, "contiguous"), (384, 64, "zigzag"), (320, 64, "striped")])
+def test_backward_large_cp_tiny_shares(S, cp, part):
+    """CP up to its limit of 64 with a few rows per rank: the ring step reaches 63,
+    and every tile of every chunk is ragged."""
+    g, gdo = bwd_case(S, 2, 1, 128, "bf16", seed=S + cp)
+    for rank in sorted({0, 1, cp // 2, cp - 1}):
+        check_rank(g, gdo, cp, rank, part)
+
+
 def test_backward_gqa_striped_cp8():
     g, gdo = bwd_case(4096, 8, 2, 128, "bf16", seed=113, docs="loguniform")
     for rank in (0, 5, 7):
