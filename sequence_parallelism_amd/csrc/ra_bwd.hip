@@ -19,12 +19,17 @@
 //    LDS, Q and dO of the lane's row in registers), then dQ^T += K^T dS^T with
 //    K^T from the transposing LDS read.
 //  * dK and dV, key-tile parallel: a workgroup owns 128 keys of one chunk and
-//    one KV head, each wave 32 keys with K and V in registers, and walks the
-//    query tiles (64 rows) that see them, for every query head of the GQA
-//    group: X = Q K^T and dP = dO V^T (Q and dO rows from LDS), then
-//    dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from the transposing
-//    read. One ring step's contribution to a chunk is exactly that chunk's
-//    key tiles, so dK / dV of chunk s are this rank's step-(rank - s) partials.
+//    one KV head and walks the query tiles (64 rows) that see them, for every
+//    query head of the GQA group: X = Q K^T and dP = dO V^T (Q and dO rows
+//    from LDS), then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from
+//    the transposing read. At head_dim 128 (ring_bwd_dkv_pp_kernel) 8 waves
+//    share the 128 keys two ways: waves w and w + 4 own the same 32 keys, take
+//    the two 32-row halves of each tile and sit on one SIMD; K and V live in
+//    LDS, and the two halves' partial dK, dV are added at the end. At head_dim
+//    64 (ring_bwd_dkv_bf16_kernel) 4 waves of 32 keys hold K and V in
+//    registers and take both halves. One ring step's contribution to a chunk
+//    is exactly that chunk's key tiles, so dK / dV of chunk s are this rank's
+//    step-(rank - s) partials.
 // Both MFMA kernels keep the lane <-> (query row or key) ownership of the
 // forward: every softmax-side quantity is a per-lane scalar or a 16-wide
 // per-lane vector, and P / dS become the next MFMA's B operand in place.
@@ -915,13 +920,309 @@ hipError_t launch_bwd_dsum(const void* out, const void* dout, float* dsum, int r
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// dK and dV, bf16 inputs, head_dim 128, two waves per SIMD. Workgroup = (key tile
+// of 128 keys of one chunk, KV head), 8 waves. Wave w owns keys 32 (w % 4) .. +31;
+// waves w and w + 4 share those keys and a SIMD, and take the two 32-row halves of
+// every 64-row query tile (group w / 4 takes rows 32 (w / 4) .. +31). K and V of the
+// workgroup's keys sit in LDS (read per product, as Q and dO are), so a wave needs
+// the dK, dV accumulators and one half's X, dP but no K, V registers. At the end,
+// the second group's partial dK, dV pass through LDS and the first group adds them
+// (a fixed order: the result is bit-reproducible).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(512, 1) ring_bwd_dkv_pp_kernel(const BwdArgs a) {
+  constexpr int D = 128;
+  constexpr int BK = kBwdBf16BK, BQ = kBwdBf16BQ;
+  static_assert(BK == 128 && BQ == 64, "tile shape is baked into the lane mapping");
+  constexpr int ROW = D;
+  constexpr int TILE = BQ * ROW, STAGE = 2 * TILE;
+  constexpr int KVT = BK * ROW;  // elements of the K (or V) tile of the workgroup's keys
+  constexpr int NCT = D / 32, NKD = D / 16;
+  // [K tile | V tile | stage 0 (Q, dO) | stage 1 (Q, dO)]; reused for the final reduction
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * KVT + 2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][BQ];  // [buf][LSE * log2 e | D][row]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wq = wave & 3;
+  const int hi32 = lane >> 5, l32 = lane & 31;
+  const int n_kt = a.cp * a.nkt_kv;
+  const int kt = a.korder[blockIdx.x / a.hkv];
+  if (kt < 0 || kt >= n_kt) return;
+  const int g = head_of_slot(blockIdx.x % a.hkv, a.hkv);
+  const int G = a.hq / a.hkv;
+  const int owner = kt / a.nkt_kv, J = kt - owner * a.nkt_kv;
+  const PartInfo pinfo{a.part, a.s_local, a.cp, a.blk};
+  const int key = J * BK + wq * 32 + l32;
+  const bool key_ok = key < a.s_local;
+  const float C = a.scale_log2;
+
+  __bf16* const ks = smem;
+  __bf16* const vs = smem + KVT;
+  __bf16* const stages = smem + 2 * KVT;
+
+  // K and V of the workgroup's 128 keys into LDS, row r chunk c at chunk slot
+  // c ^ swz_rt(r) (keys past the end read as zeros through the buffer bound)
+  const uint32_t kv_row_bytes = (uint32_t)a.hkv * D * 2u;
+  const uint32_t chunk_bytes = (uint32_t)a.s_local * kv_row_bytes;
+  {
+    const size_t cbase = (size_t)owner * chunk_bytes;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc((const char*)a.k + cbase, chunk_bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc((const char*)a.v + cbase, chunk_bytes);
+#pragma unroll
+    for (int i = 0; i < (BK * D / 8) / 512; ++i) {
+      const int c = tid + 512 * i;  // 16-byte chunk of the tile
+      const int r = c >> 4, c8 = c & 15;
+      const uint32_t off = (uint32_t)(J * BK + r) * kv_row_bytes + (uint32_t)g * D * 2u + 16u * c8;
+      const uint4 kv = buffer_load16(kr, off), vv = buffer_load16(vr, off);
+      const int slot = r * ROW + 8 * (c8 ^ swz_rt(r));
+      *(uint4*)(ks + slot) = kv;
+      *(uint4*)(vs + slot) = vv;
+    }
+  }
+  int plo = 1, phi = 0;  // visible query positions of this key
+  if (key_ok) key_interval(a.cu, a.n_docs, a.s_total, a.causal, pos_of(pinfo, owner, key), plo, phi);
+
+  f32x16 dk[NCT], dv[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) dk[c] = dv[c] = f32x16{};
+
+  const int n_ent = clamp_count(a.kwl_count[kt], a.kwl_stride);
+  const int* list = a.kwl + (size_t)kt * a.kwl_stride;
+  const int total = n_ent * G;
+  const uint32_t q_row_bytes = (uint32_t)a.hq * D * 2u;
+  const uint32_t q_bytes = (uint32_t)a.s_local * q_row_bytes;
+  // this wave's tile source: Q for the first group, dO for the second
+  const __amdgpu_buffer_rsrc_t mrs = buffer_rsrc(grp ? a.dout : a.q, q_bytes);
+
+  // direct loads: waves 0-3 fill the Q tile, waves 4-7 the dO tile, 16 rows each
+  uint32_t d_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wq + 4 * i + (lane >> 4), pc = lane & 15;
+    d_off[i] = (uint32_t)r * q_row_bytes + 8u * (pc ^ swz_rt(r)) * 2u;
+  }
+  float rl = 0.f, rd = 0.f;
+  bool rok = false;
+  auto load_tile = [&](int hh, int ent, int buf) {
+    const int h = g * G + hh, I = wl_tile(ent);
+    const uint32_t toff = (uint32_t)I * BQ * q_row_bytes + (uint32_t)h * D * 2u;
+    __attribute__((address_space(3))) char* dl =
+        (__attribute__((address_space(3))) char*)(stages + buf * STAGE + grp * TILE) + 4096 * wq;
+    const uint32_t db = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)dl);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16_lds(mrs, toff + d_off[i], db + 1024u * i);
+    if (wave == 0) {
+      const int r = I * BQ + opaque(lane);
+      rok = r < a.s_local && I < a.nqt_kv;
+      const size_t idx = rok ? (size_t)h * a.s_local + r : 0;
+      rl = a.lse[idx];
+      rd = a.dsum[idx];
+    }
+  };
+  auto store_tile = [&](int buf) {
+    __builtin_amdgcn_s_waitcnt(0);
+    if (wave == 0) {
+      const int ln = opaque(lane);
+      rowv[buf][0][ln] = rok && rl != -INFINITY ? rl * kLog2e : INFINITY;
+      rowv[buf][1][ln] = rok ? rd : 0.f;
+    }
+  };
+
+  // per-lane LDS element offsets (see the one-wave kernel): row-wise reads of row
+  // l32 at logical chunk 2 j + hi32, transposing reads of rows 4 hi32 + (lane%16)/4
+  // and 8 more at columns 32 c + 16 ((lane/16)%2) + 4 (lane%4)
+  int rd_off[NKD], tr0_off[NCT], tr1_off[NCT];
+#pragma unroll
+  for (int j = 0; j < NKD; ++j) rd_off[j] = l32 * ROW + 8 * ((2 * j + hi32) ^ swz_rt(l32));
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    const int r0 = 4 * hi32 + ((lane & 15) >> 2);
+    const int c0 = c * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    tr0_off[c] = r0 * ROW + ((((c0 >> 3) ^ swz_rt(r0)) << 3) | (c0 & 7));
+    tr1_off[c] = (r0 + 8) * ROW + ((((c0 >> 3) ^ swz_rt(r0 + 8)) << 3) | (c0 & 7));
+  }
+
+  ListWindow<true> wl;
+  wl.init(list, n_ent, lane);
+  if (total > 0) {
+    load_tile(0, wl.get(0), 0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  int hh = 0, idx = 0;
+  for (int it = 0; it < total; ++it) {
+    const int ent = wl.get(idx);
+    const int I = wl_tile(ent), cls = wl_cls(ent);
+    const bool ent_ok = I < a.nqt_kv && cls != CLS_SKIP;
+    const bool wrap = idx + 1 == n_ent;
+    if (it + 1 < total) load_tile(wrap ? hh + 1 : hh, wl.get(wrap ? 0 : idx + 1), (it + 1) & 1);
+
+    // this group's 32-row half of the tile
+    const int qa = I * BQ;
+    const int qb = qa + BQ < a.s_local ? qa + BQ : a.s_local;
+    bool need_mask = qb - qa < BQ || cls == CLS_PARTIAL;
+    bool do_tile = ent_ok;
+    TileMask tm{0, BQ, 0, 0};
+    if (do_tile && need_mask) {
+      tm = tile_mask(pinfo, a.rank, qa, qb, cls, key_ok, plo, phi);
+      do_tile = __any(tm.la > 0 || tm.lb > 0);
+      need_mask = !__all(tile_all_visible(tm, BQ) || !key_ok);
+    }
+
+    if (do_tile) {
+      const int buf = it & 1;
+      const __bf16* qs = stages + buf * STAGE;
+      const __bf16* os = qs + TILE;
+      const int qh = grp;
+      const __bf16* qh_q = qs + qh * 32 * ROW;
+      const __bf16* qh_o = os + qh * 32 * ROW;
+      const float* l2s = rowv[buf][0];
+      const float* dss = rowv[buf][1];
+      f32x16 x = f32x16{}, dp = f32x16{};
+      f32x4 Lr[4], Dr[4];
+      __builtin_amdgcn_s_setprio(1);
+      // the key-side base kept opaque: the per-read addresses are then formed at each
+      // use (one add) instead of being hoisted out of the loop into registers
+      const int kvo = opaque(wq * 32 * ROW);
+#pragma unroll
+      for (int j = 0; j < NKD; ++j) {
+        const bf16x8 kf = *(const bf16x8*)(ks + kvo + rd_off[j]);
+        const bf16x8 vf = *(const bf16x8*)(vs + kvo + rd_off[j]);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qh_q + rd_off[j]), kf, x, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qh_o + rd_off[j]), vf, dp, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        Lr[i4] = *(const f32x4*)(l2s + qh * 32 + 8 * i4 + 4 * hi32);
+        Dr[i4] = *(const f32x4*)(dss + qh * 32 + 8 * i4 + 4 * hi32);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_s_setprio(0);
+      if (!need_mask) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 L = Lr[i4], Dd = Dr[i4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * i4 + u;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], C, -L[u]));
+            x[i] = p;
+            dp[i] = p * (dp[i] - Dd[u]);
+          }
+        }
+      } else {
+        const int ba = 4 * hi32 - tm.i0a, bb = 4 * hi32 - tm.i0b;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 L = Lr[i4], Dd = Dr[i4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * i4 + u, n = qh * 32 + 8 * i4 + u;
+            const bool vis = ((unsigned)(n + ba) < (unsigned)tm.la) | ((unsigned)(n + bb) < (unsigned)tm.lb);
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], C, -L[u])) : 0.f;
+            x[i] = p;
+            dp[i] = vis ? p * (dp[i] - Dd[u]) : 0.f;
+          }
+        }
+      }
+      const bf16x8 pb0 = __builtin_convertvector(x.lo, bf16x8), pb1 = __builtin_convertvector(x.hi, bf16x8);
+      const bf16x8 sb0 = __builtin_convertvector(dp.lo, bf16x8), sb1 = __builtin_convertvector(dp.hi, bf16x8);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int ro = jj * 16 * ROW;
+          const bf16x8 ot = __builtin_shufflevector(lds_read_tr(qh_o + ro + tr0_off[c]),
+                                                    lds_read_tr(qh_o + ro + tr1_off[c]), 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 qt8 = __builtin_shufflevector(lds_read_tr(qh_q + ro + tr0_off[c]),
+                                                     lds_read_tr(qh_q + ro + tr1_off[c]), 0, 1, 2, 3, 4, 5, 6, 7);
+          dv[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, jj ? pb1 : pb0, dv[c], 0, 0, 0);
+          dk[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt8, jj ? sb1 : sb0, dk[c], 0, 0, 0);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_s_setprio(0);
+    }
+
+    if (it + 1 < total) store_tile((it + 1) & 1);
+    __syncthreads();
+    if (wrap) {
+      wl.restart(lane);
+      idx = 0;
+      ++hh;
+    } else {
+      wl.advance(idx, lane);
+      ++idx;
+    }
+  }
+
+  // the second group's partials through LDS (2 x 4 x 16 floats per lane = 32 KiB per
+  // wave, 128 KiB for the group: the whole of the K, V and stage space)
+  __syncthreads();
+  float* red = (float*)smem;
+  if (grp == 1) {
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[((wq * 2 * NCT + c) * 16 + i) * 64 + lane] = dk[c][i];
+        red[((wq * 2 * NCT + NCT + c) * 16 + i) * 64 + lane] = dv[c][i];
+      }
+  }
+  __syncthreads();
+  if (grp == 0 && key_ok) {
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dk[c][i] += red[((wq * 2 * NCT + c) * 16 + i) * 64 + lane];
+        dv[c][i] += red[((wq * 2 * NCT + NCT + c) * 16 + i) * 64 + lane];
+      }
+    const size_t base = (((size_t)owner * a.s_local + key) * a.hkv + g) * D;
+    // the output pointers are read from the argument segment here (a volatile load),
+    // not kept in scalar registers through the loop
+    typedef __attribute__((address_space(4))) const BwdArgs KArgs;
+    KArgs* ka = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    float* const dkp = *(float* const volatile __attribute__((address_space(4)))*)&ka->dk;
+    float* const dvp = *(float* const volatile __attribute__((address_space(4)))*)&ka->dv;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = c * 32 + 8 * i4 + 4 * hi32;
+        *(f32x4*)(dkp + base + col) =
+            f32x4{dk[c][4 * i4], dk[c][4 * i4 + 1], dk[c][4 * i4 + 2], dk[c][4 * i4 + 3]} * a.scale;
+        *(f32x4*)(dvp + base + col) = f32x4{dv[c][4 * i4], dv[c][4 * i4 + 1], dv[c][4 * i4 + 2], dv[c][4 * i4 + 3]};
+      }
+  }
+}
+
 template <int D>
 static hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((ring_bwd_dq_bf16_kernel<D>), dim3((unsigned)a.nqt * (unsigned)a.hq), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ring_bwd_dkv_bf16_kernel<D>), dim3((unsigned)(a.cp * a.nkt_kv) * (unsigned)a.hkv), dim3(256), 0,
-                     st, a);
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL(ring_bwd_dkv_pp_kernel, dim3((unsigned)(a.cp * a.nkt_kv) * (unsigned)a.hkv), dim3(512), 0, st,
+                       a);
+  } else {
+    hipLaunchKernelGGL((ring_bwd_dkv_bf16_kernel<D>), dim3((unsigned)(a.cp * a.nkt_kv) * (unsigned)a.hkv), dim3(256),
+                       0, st, a);
+  }
   return hipGetLastError();
 }
 
