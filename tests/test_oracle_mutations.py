@@ -4,7 +4,8 @@ unnormalised merge weights, a reversed ring) and in the backward (a dropped D
 term, a flipped sign, a wrong operand or scale, a gradient off by 1e-4, GQA
 groups not summed) and in the layouts (Ulysses head or token order, a reorder
 inverse off by a rank, ragged tiles, the per-document zigzag's bounds and pair
-rotation) is put into the oracle by monkeypatching, and at least one of its pins
+rotation) and in the Ulysses x Ring hybrid (head slices, key positions) is put
+into the oracle by monkeypatching, and at least one of its pins
 must then fail. Without a planted mistake every pin passes.
 
 The mistakes are planted in the oracle only, on the CPU. The pins compare it with
@@ -332,3 +333,59 @@ def test_planted_layout_mistake_fails_a_pin(mistake, monkeypatch):
     for module, name, fn in LAYOUT_MISTAKES[mistake]:
         monkeypatch.setattr(module, name, fn)
     assert _failing_layout_pins(), f"no pin notices: {mistake}"
+
+
+# ---------------------------------------------------------------------------
+# The Ulysses x Ring hybrid: usp_forward restated with one slip each.
+# ---------------------------------------------------------------------------
+import oracle.usp as usp_mod  # noqa: E402
+from tests import test_oracle_usp as usp_pins  # noqa: E402
+
+
+def _usp_with(slip):
+    def f(gq, gk, gv, cu_seqlens, U, R, partition, causal=True, scale=None):
+        S, hq, d = gq.shape
+        sl = S // R
+        Yq = [lay_mod.ulysses_permute(s, U) for s in usp_mod.usp_device_shards(gq, U, R, partition)]
+        Yk = [lay_mod.ulysses_permute(s, U) for s in usp_mod.usp_device_shards(gk, U, R, partition)]
+        Yv = [lay_mod.ulysses_permute(s, U) for s in usp_mod.usp_device_shards(gv, U, R, partition)]
+        pos = [part_mod.positions(partition, S, R, r) for r in range(R)]
+        O = np.zeros((R, U, sl, hq // U, d))
+        L = np.full((R, U, hq // U, sl), -np.inf)
+        for r in range(R):
+            for u in range(U):
+                o = lse = None
+                for s in att.ring_chunk_order(R, r):
+                    uk = (U - 1 - u) if slip == "KV head slice mirrored" else u
+                    pk = pos[r] if slip == "key positions of the query group" else pos[s]
+                    o_t, l_t = _orig_rows(Yq[r][u], pos[r], Yk[s][uk], Yv[s][uk], pk, cu_seqlens, S, causal, scale)
+                    o, lse = (o_t, l_t) if o is None else _orig_merge(o, lse, o_t, l_t)
+                O[r, u], L[r, u] = o, lse
+        out = np.stack([lay_mod.ulysses_permute(O[r], U, inverse=True) for r in range(R)])
+        return out, L
+    return f
+
+
+USP_SLIPS = [None, "KV head slice mirrored", "key positions of the query group"]
+USP_PINS = {
+    "global attention, U = R = 2, zigzag with documents": lambda: usp_pins.test_usp_equals_global_attention(
+        2, 2, "zigzag", True),
+    "global attention, U = 4, R = 2, striped": lambda: usp_pins.test_usp_equals_global_attention(4, 2, "striped", False),
+    "corner cases": usp_pins.test_usp_corner_cases_reduce_to_ring_and_ulysses,
+}
+
+
+@pytest.mark.parametrize("slip", USP_SLIPS)
+def test_planted_usp_slip_fails_a_pin(slip, monkeypatch):
+    monkeypatch.setattr(usp_mod, "usp_forward", _usp_with(slip))
+    monkeypatch.setattr(oracle, "usp_forward", _usp_with(slip))
+    failed = []
+    for name, pin in USP_PINS.items():
+        try:
+            pin()
+        except AssertionError:
+            failed.append(name)
+    if slip is None:
+        assert failed == [], failed  # the restatement without a slip passes every pin
+    else:
+        assert failed, f"no pin notices: {slip}"
