@@ -31,7 +31,9 @@ CUS = {
 
 
 @pytest.mark.parametrize("name,cp,h,d,elem", [("one", 4, 2, 128, 2), ("three", 8, 3, 64, 2),
-                                              ("many", 2, 1, 5, 4), ("many", 3, 2, 128, 2)])
+                                              ("many", 2, 1, 5, 4), ("many", 3, 2, 128, 2),
+                                              ("three", 4, 64, 128, 2), ("many", 3, 1, 8, 2),
+                                              ("one", 2, 8, 128, 4)])
 def test_reorder_docs_bit_exact(name, cp, h, d, elem):
     cu = CUS[name]
     S = 2048 if cu is None else int(cu[-1])
