@@ -244,7 +244,7 @@ def main():
     ap.add_argument("--rank", type=int, default=None, help="attn-only: the rank (default: the headline rank; -1: every rank in turn)")
     ap.add_argument("--which", default="ulysses_fwd",
                     choices=["ulysses_fwd", "ulysses_inv", "reorder_llama7b", "reorder_gqa_q", "reorder_gqa_kv",
-                             "reorder_packed", "reorder_docs"])
+                             "reorder_packed", "reorder_docs", "merge"])
     ap.add_argument("--launches", type=int, default=12, help="launches in the single-kernel modes")
     args = ap.parse_args()
 
@@ -463,6 +463,13 @@ def permute_only(np, torch, ra, synth, dev, which, launches):
         else:
             fn = lambda: ra.ulysses_permute(y, U_N, inverse=True, out=x)  # noqa: E731
         nbytes = 2 * x.numel() * 2
+    elif which == "merge":
+        oa = torch.randn((8192, 32, 128), device=dev, generator=gen)
+        ob, oo = torch.randn_like(oa), torch.empty_like(oa)
+        la, lb = torch.randn((32, 8192), device=dev, generator=gen), torch.randn((32, 8192), device=dev, generator=gen)
+        lo = torch.empty_like(la)
+        fn = lambda: ra.ra_lse_merge(oa, la, ob, lb, o_out=oo, lse_out=lo)  # noqa: E731
+        nbytes = 3 * oa.numel() * 4 + 3 * la.numel() * 4
     elif which == "reorder_docs":
         w = synth.PACKED_ZIGZAG
         cu = synth.loguniform_cu_seqlens(0, w.s_total, w.doc_lo, w.doc_hi)
