@@ -60,6 +60,27 @@ def max_abs(a, b):
     return float(np.max(d)) if d.size else 0.0
 
 
+def bf16_half_ulp(x):
+    """Half a unit in the last place of bf16 (8 significant bits) at |x|: the most
+    that one round-to-nearest store to bf16 moves a value of that magnitude."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(x)  # |x| = m 2^e with m in [0.5, 1), so the bf16 ulp is 2^(e - 8)
+    return np.where(x > 0, np.ldexp(1.0, e - 9), 0.0)
+
+
+def o_err(o, O, out_bf16=False):
+    """Max-abs error of an attention output against the oracle. The bar applies to
+    the arithmetic; a bf16 output is that result rounded once more by the store,
+    so up to half a bf16 ulp of the value is taken off each element's error first.
+    An unwritten (NaN) element still fails."""
+    o = np.asarray(o, dtype=np.float64)
+    O = np.asarray(O, dtype=np.float64)
+    d = np.abs(o - O)
+    if out_bf16:
+        d = np.maximum(d - bf16_half_ulp(np.maximum(np.abs(o), np.abs(O))), 0.0)
+    return float(np.max(d)) if d.size else 0.0
+
+
 def sample_rows(s_local: int, extra=(), n_random: int = 24, seed: int = 0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     rows = {0, 1, s_local // 2 - 1, s_local // 2, s_local - 2, s_local - 1}

@@ -16,7 +16,7 @@ import torch
 import oracle
 import sequence_parallelism_amd as ra
 import synth
-from tests.gpu_common import (TOL_LSE_BF16, TOL_LSE_F32, TOL_O_BF16, TOL_O_F32, max_abs, oracle_inputs,
+from tests.gpu_common import (TOL_LSE_BF16, TOL_LSE_F32, TOL_O_BF16, TOL_O_F32, max_abs, o_err, oracle_inputs,
                               rank_inputs, sample_rows, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -43,7 +43,7 @@ def _check_rank(g, cp, rank, part, causal=True, rows=None, out_dtype=torch.float
     if tol_o is None:
         tol_o = TOL_O_BF16 if g.dtype == "bf16" else TOL_O_F32
         tol_l = TOL_LSE_BF16 if g.dtype == "bf16" else TOL_LSE_F32
-    eo, el = max_abs(o, O), max_abs(l, L)
+    eo, el = o_err(o, O, out_dtype == torch.bfloat16), max_abs(l, L)
     assert np.all(np.isfinite(o)), "non-finite output"
     assert eo <= tol_o and el <= tol_l, f"max-abs O {eo:.3e} LSE {el:.3e}"
     return eo, el
