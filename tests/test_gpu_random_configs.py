@@ -6,9 +6,11 @@ heads with GQA ratio 1, 2 or 4, CP from 1 to 8 (odd sizes included), any
 partition including per-document zigzag, packed documents or one sequence,
 causal or document-only masks, a default or explicit softmax scale, fp32 or
 bf16 output, and a few fp32-input cases. Local lengths are random, so tiles are
-ragged. Ranks 0 and CP-1 are checked on every row against the fp64 oracle at
-the usual bars (max-abs 1e-2 on O and 1e-3 on LSE for bf16 inputs, 1e-4 for
-fp32 inputs; the backward's derived per-element bound).
+ragged. A second set of edge draws takes local lengths from a single row, CP up
+to the 64-rank maximum (odd and prime sizes among them) and up to 64 query heads.
+Ranks 0 and CP-1 are checked on every row against the fp64 oracle at the usual
+bars (max-abs 1e-2 on O, after a bf16 output's store rounding, and 1e-3 on LSE for
+bf16 inputs; 1e-4 for fp32 inputs; the backward's derived per-element bound).
 """
 import numpy as np
 import pytest
@@ -46,7 +48,29 @@ def _draw(i):
                 out_bf16=out_bf16 and dtype == "bf16", dtype=dtype, seed=1000 + i)
 
 
-CONFIGS = [_draw(i) for i in range(64)]
+def _draw_edge(i):
+    """Edge draws: local lengths from 1 row, CP up to the 64-rank maximum (odd and
+    prime sizes included), up to 64 query heads."""
+    rng = np.random.default_rng(777000 + i)
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 3, 8, 16]))
+    hq = min(hkv * int(rng.choice([1, 2, 4, 8])), 64)
+    hkv = hq // max(1, hq // hkv)
+    cp = int(rng.choice([1, 2, 6, 7, 12, 16, 31, 32, 64]))
+    part = PARTS[int(rng.integers(0, 4))]
+    unit = 2 * cp if part == "zigzag" else cp
+    s_l = int(rng.integers(1, 40)) if rng.random() < 0.6 else int(rng.integers(40, 300))
+    S = min(max(unit, (s_l * cp // unit) * unit), max(unit, (6000 // unit) * unit))
+    docs = part == "doc_zigzag" or rng.random() < 0.5
+    causal = bool(rng.random() < 0.75)
+    scale = float(rng.uniform(0.04, 0.2)) if rng.random() < 0.3 else 0.0
+    out_bf16 = bool(rng.random() < 0.3)
+    dtype = "f32" if rng.random() < 0.1 else "bf16"
+    return dict(d=d, hq=hq, hkv=hkv, cp=cp, part=part, S=S, docs=docs, causal=causal, scale=scale,
+                out_bf16=out_bf16 and dtype == "bf16", dtype=dtype, seed=5000 + i)
+
+
+CONFIGS = [_draw(i) for i in range(64)] + [_draw_edge(i) for i in range(48)]
 
 
 def _inputs(c):
@@ -86,7 +110,7 @@ def test_forward_random_config(c):
             assert np.all(np.isfinite(o)) and not np.any(np.isnan(l))
 
 
-BWD_CONFIGS = [c for c in CONFIGS if not c["scale"]][:20]
+BWD_CONFIGS = [c for c in CONFIGS[:64] if not c["scale"]][:20] + [c for c in CONFIGS[64:] if not c["scale"]][:16]
 
 
 @pytest.mark.parametrize("c", BWD_CONFIGS, ids=_label)
