@@ -11,6 +11,9 @@ to the 64-rank maximum (odd and prime sizes among them) and up to 64 query heads
 Ranks 0 and CP-1 are checked on every row against the fp64 oracle at the usual
 bars (max-abs 1e-2 on O, after a bf16 output's store rounding, and 1e-3 on LSE for
 bf16 inputs; 1e-4 for fp32 inputs; the backward's derived per-element bound).
+Random Ulysses x Ring grids go through usp_forward against oracle.usp_forward, and
+the per-step partials of ra_forward_steps, folded with ra_lse_merge, against the
+oracle's step partials and whole-ring rows.
 """
 import numpy as np
 import pytest
@@ -22,7 +25,7 @@ import synth
 from oracle.partition import positions
 from tests.bwd_common import check_rank as check_backward_rank
 from tests.gpu_common import (TOL_LSE_BF16, TOL_LSE_F32, TOL_O_BF16, TOL_O_F32, max_abs, o_err, oracle_inputs,
-                              rank_inputs)
+                              rank_inputs, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,3 +126,76 @@ def test_backward_random_config(c):
     for rank in sorted({0, c["cp"] - 1}):
         print(f"[random-config backward] {_label(c)} rank {rank}", flush=True)
         check_backward_rank(g, gdo, c["cp"], rank, c["part"], causal=c["causal"], out_dtype=out_dtype, **kw)
+
+
+def _draw_usp(i):
+    rng = np.random.default_rng(884000 + i)
+    U, R = int(rng.choice([1, 2, 3, 4, 8])), int(rng.choice([1, 2, 3, 4]))
+    part = ("contiguous", "zigzag", "striped")[int(rng.integers(0, 3))]
+    hkv = U * int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    unit = R * U * (2 if part == "zigzag" else 1)
+    S = unit * int(rng.integers(1, max(2, 2400 // unit)))
+    return dict(U=U, R=R, part=part, hq=hq, hkv=hkv, d=int(rng.choice([64, 128])), S=S,
+                docs=bool(rng.random() < 0.5), dtype="f32" if rng.random() < 0.15 else "bf16",
+                out_bf16=bool(rng.random() < 0.3), seed=6000 + i)
+
+
+USP_CONFIGS = [_draw_usp(i) for i in range(24)]
+
+
+def _usp_label(c):
+    return (f"{c['part']}-u{c['U']}-r{c['R']}-S{c['S']}-h{c['hq']}x{c['hkv']}-d{c['d']}-{c['dtype']}"
+            f"{'-docs' if c['docs'] else ''}{'-bf16out' if c['out_bf16'] and c['dtype'] == 'bf16' else ''}")
+
+
+@pytest.mark.parametrize("c", USP_CONFIGS, ids=_usp_label)
+def test_usp_random_config(c):
+    """The Ulysses x Ring grid: every device's output and LSE against oracle.usp_forward."""
+    w = synth.Workload("random_usp", c["S"], c["hq"], c["hkv"], c["d"], 1, "contiguous", 0, c["dtype"],
+                       docs="loguniform" if c["docs"] else None, doc_lo=8, doc_hi=max(9, c["S"] // 2))
+    g = synth.make_global_inputs(w, c["seed"])
+    U, R, part, S = c["U"], c["R"], c["part"], c["S"]
+    out_bf16 = c["out_bf16"] and c["dtype"] == "bf16"
+    print(f"[random-config usp] {_usp_label(c)}", flush=True)
+    q, k, v = (ra.cp_reorder(to_device(x, g.dtype), R, part).view(R, U, S // (R * U), x.shape[1], x.shape[2])
+               for x in (g.q, g.k, g.v))
+    out, lse = ra.usp_forward(q, k, v, g.cu_seqlens, U, R, part,
+                              out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    gq, gk, gv = oracle_inputs(g)
+    O, L = oracle.usp_forward(gq, gk, gv, g.cu_seqlens, U, R, part)
+    tol_o, tol_l = (TOL_O_BF16, TOL_LSE_BF16) if c["dtype"] == "bf16" else (TOL_O_F32, TOL_LSE_F32)
+    eo = o_err(out.float().cpu().numpy(), O, out_bf16)
+    el = max_abs(np.transpose(lse.cpu().numpy(), (1, 0, 2, 3)), L)
+    assert eo <= tol_o and el <= tol_l, f"max-abs O {eo:.3e} LSE {el:.3e}"
+
+
+STEPS_CONFIGS = [c for c in CONFIGS if c["cp"] > 1][:24]
+
+
+@pytest.mark.parametrize("c", STEPS_CONFIGS, ids=_label)
+def test_steps_and_merge_random_config(c):
+    """Per-step partials against the oracle's, and their LSE-merge fold against the
+    oracle's whole-ring rows."""
+    g = _inputs(c)
+    cp, part = c["cp"], c["part"]
+    rank = cp - 1
+    tol_o, tol_l = (TOL_O_BF16, TOL_LSE_BF16) if c["dtype"] == "bf16" else (TOL_O_F32, TOL_LSE_F32)
+    print(f"[random-config steps] {_label(c)} rank {rank}", flush=True)
+    qr, kr, vr = rank_inputs(g, cp, rank, part)
+    o_steps, lse_steps = ra.ra_forward_steps(qr, kr, vr, g.cu_seqlens, cp, rank, part, causal=c["causal"],
+                                             softmax_scale=c["scale"],
+                                             s_total=c["S"] if part == "doc_zigzag" else None)
+    torch.cuda.synchronize()
+    gq, gk, gv = oracle_inputs(g)
+    for t, (_, O_t, L_t) in enumerate(oracle.step_partials(gq, gk, gv, g.cu_seqlens, cp, rank, part, c["causal"],
+                                                           scale=c["scale"] or None)):
+        eo, el = max_abs(o_steps[t].cpu().numpy(), O_t), max_abs(lse_steps[t].cpu().numpy(), L_t)
+        assert eo <= tol_o and el <= tol_l, f"step {t}: max-abs O {eo:.3e} LSE {el:.3e}"
+    o, l = o_steps[0].clone(), lse_steps[0].clone()
+    for t in range(1, cp):
+        o, l = ra.ra_lse_merge(o, l, o_steps[t], lse_steps[t], o_out=o, lse_out=l)
+    O, L = oracle.attention_rank(gq, gk, gv, g.cu_seqlens, cp, rank, part, c["causal"], scale=c["scale"] or None)
+    eo, el = max_abs(o.cpu().numpy(), O), max_abs(l.cpu().numpy(), L)
+    assert eo <= tol_o and el <= tol_l, f"merged: max-abs O {eo:.3e} LSE {el:.3e}"
