@@ -52,9 +52,9 @@ def _sample_keys(pos, cu, S, seed, n_few=8, n_none=4, max_view=48):
     return np.array(sorted(int(x) for x in pick)), ps, order
 
 
-def _fullsize(w, rank, rows, seed):
-    g = synth.make_global_inputs(w, 0)
-    gdo = synth.make_global_dout(w, 0)
+def _fullsize(w, rank, rows, seed, input_seed=0):
+    g = synth.make_global_inputs(w, input_seed)
+    gdo = synth.make_global_dout(w, input_seed)
     cp, part, S = w.cp, w.partition, w.s_total
     qr, kr, vr = rank_inputs(g, cp, rank, part)
     out, lse = ra.ra_forward(qr, kr, vr, g.cu_seqlens, cp, rank, part, out_dtype=torch.bfloat16)
@@ -96,6 +96,7 @@ def _fullsize(w, rank, rows, seed):
         check_bound("dk", got_k[idx], ref.dk[kp], REL * ref.A_dk[kp] + xk[kp] + SLACK)
         check_bound("dv", got_v[idx], ref.dv[kp], REL * ref.A_dv[kp] + SLACK)
     assert np.all(np.isfinite(dq.cpu().numpy())) and np.all(np.isfinite(dk.cpu().numpy()))
+    assert np.all(np.isfinite(dv.cpu().numpy()))
     return len(seen), len(unseen)
 
 
@@ -114,9 +115,12 @@ def test_backward_gqa_striped_sampled():
     assert n_seen > 0
 
 
-def test_backward_packed_documents_sampled():
+@pytest.mark.parametrize("input_seed", [0, 1])
+def test_backward_packed_documents_sampled(input_seed):
+    """Two document layouts (input seeds 0 and 1) of the packed workload."""
     w = synth.PACKED_ZIGZAG
-    for rank in (0, 5):
+    for rank in ((0, 5) if input_seed == 0 else (7,)):
         rows = sample_rows(w.s_total // w.cp, n_random=8, seed=10 + rank)
-        n_seen, _ = _fullsize(w, rank, rows, seed=10 + rank)
+        print(f"packed backward input seed {input_seed} rank {rank}", flush=True)
+        n_seen, _ = _fullsize(w, rank, rows, seed=10 + rank, input_seed=input_seed)
         assert n_seen > 0
